@@ -1,0 +1,195 @@
+"""Pins for the oracle's block scores (CPU only).
+
+What the oracle computes (page "vllm.models.minimax_m3.amd.ops.index_topk",
+module docstring and minimax_m3_index_score docstring): for every query row
+and visible 128-token block, the maximum over the block's causally visible
+tokens of sm_scale * (q . k), with one shared key per token.
+
+Pins, none of which re-types the oracle:
+  * a numpy float64 matmul over the flattened, de-paged context with a causal
+    mask and a reshape-amax per 128 keys (a different algorithm);
+  * torch CPU float32 matmul + amax, within float32 error;
+  * a closed form for the partial last block (monotone keys);
+  * invariances: poisoned unread slots, page permutation, power-of-two
+    sm_scale, head permutation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import KFMT_BF16, KFMT_NVFP4, cdiv, host_arrays, make
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _keys_f64(a, page_ids):
+    """[n_pages, 128, 128] float64 keys of the given pages."""
+    if a["kfmt"] == KFMT_BF16:
+        return _bf16_to_f64(a["kdata"][page_ids])
+    nb = a["kdata"][page_ids].astype(np.int64)
+    nib = np.stack([nb & 15, nb >> 4], axis=-1).reshape(nb.shape[0], 128, 128)
+    sc = np.repeat(a["kscales"][page_ids], 16, axis=-1)
+    # dequant through the oracle's scalar codec would not be independent; use
+    # torch's e4m3 decode, the E2M1 table and torch's fp8 cast for rounding
+    sv = torch.from_numpy(sc.astype(np.uint8).copy()).view(torch.float8_e4m3fn).double()
+    mag = torch.tensor(E2M1, dtype=torch.float64)[torch.from_numpy(nib & 7)]
+    sgn = torch.where(torch.from_numpy(nib & 8) > 0, -1.0, 1.0).double()
+    # satfinite: clamp to +-448 first (only poison slots reach it here)
+    prod = (mag * sgn * sv).float().clamp(-448.0, 448.0)
+    return prod.to(torch.float8_e4m3fn).double().numpy()
+
+
+def brute_scores(a, width):
+    q = _bf16_to_f64(a["q_bits"])
+    T, H, _ = q.shape
+    Q = a["query_len"]
+    out = np.full((H, T, width), np.nan, dtype=np.float32)
+    for r, L in enumerate(a["seq_lens"]):
+        nb = cdiv(int(L), 128)
+        if nb == 0:
+            continue
+        K = _keys_f64(a, a["block_table"][r, :nb]).reshape(nb * 128, 128)
+        for j in range(Q):
+            t = r * Q + j
+            pos = int(L) - Q + j
+            if pos < 0:
+                continue
+            nv = pos // 128 + 1
+            dots = q[t] @ K[: nv * 128].T  # [H, nv*128]
+            dots[:, pos + 1:] = -np.inf
+            m = dots.reshape(H, nv, 128).max(-1)
+            out[:, t, :nv] = (a["sm_scale"] * m).astype(np.float32)
+    return out
+
+
+def _small(seed, kfmt=KFMT_BF16, R=3, lens=(1, 700), Q=4, H=2, msl=1024, **kw):
+    return make(name="t", R=R, lens=lens, Q=Q, H=H, max_seq_len=msl, topk=4,
+                I=1, L=1, kfmt=kfmt, seed=seed, device="cpu", **kw)
+
+
+def _oracle_scores(a, width, rows=None):
+    return oracle.block_scores(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"],
+                               a["block_table"], a["seq_lens"], a["query_len"],
+                               a["sm_scale"], width, rows=rows)
+
+
+def _same(x, y, rtol=0.0, atol=0.0):
+    vis = ~np.isnan(y)
+    assert np.array_equal(np.isnan(x), np.isnan(y))
+    np.testing.assert_allclose(x[vis], y[vis], rtol=rtol, atol=atol)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("kfmt", [KFMT_BF16, KFMT_NVFP4])
+def test_vs_numpy_float64(seed, kfmt):
+    w = _small(seed, kfmt=kfmt)
+    a = host_arrays(w)
+    _same(_oracle_scores(a, w.score_width), brute_scores(a, w.score_width), rtol=1e-6, atol=1e-6)
+
+
+def test_vs_torch_fp32_special_case():
+    """One request, one head: scores equal torch fp32 q@K^T, masked, amax
+    over 128 keys, times sm_scale (fp32 rounding error only)."""
+    w = _small(11, R=1, lens=(900, 900), Q=8, H=1)
+    a = host_arrays(w)
+    got = _oracle_scores(a, w.score_width)
+    q = w.q.float()[:, 0]  # [8, 128]
+    nb = cdiv(900, 128)
+    K = w.kdata[w.block_table[0, :nb].long()].float().reshape(-1, 128)
+    s = q @ K.T
+    pos = torch.arange(900 - 8, 900)
+    s[torch.arange(s.shape[1])[None, :] > pos[:, None]] = -float("inf")
+    m = s.reshape(8, nb, 128).amax(-1) * w.sm_scale
+    for j in range(8):
+        nv = int(pos[j]) // 128 + 1
+        np.testing.assert_allclose(got[0, j, :nv], m[j, :nv].numpy(), rtol=2e-5, atol=2e-5)
+
+
+def test_partial_block_closed_form():
+    """q = c e0 and key[0] strictly increasing with the slot in the block
+    (1 + s/128, exact in bf16): the block score is sm_scale * c * key[0] of
+    the last visible token."""
+    L, Q = 1000, 4
+    w = _small(5, R=1, lens=(L, L), Q=Q, H=1)
+    c = 2.0
+    w.q.zero_()
+    w.q[:, 0, 0] = c
+    bt = w.block_table[0]
+    for p in range(L):
+        w.kdata[bt[p // 128], p % 128, 0] = 1.0 + (p % 128) / 128.0
+    a = host_arrays(w)
+    got = _oracle_scores(a, w.score_width)
+    for j in range(Q):
+        pos = L - Q + j
+        for b in range(pos // 128 + 1):
+            last = min(pos, 128 * b + 127)
+            # sm_scale crosses the boundary as an fp32 value
+            want = float(np.float32(w.sm_scale)) * c * (1.0 + (last - 128 * b) / 128.0)
+            assert got[0, j, b] == np.float32(want)
+
+
+def test_poisoned_unread_slots_change_nothing():
+    w = _small(6)
+    a = host_arrays(w)
+    base = _oracle_scores(a, w.score_width)
+    # overwrite every slot that no visible block covers with a huge value
+    kd = a["kdata"].copy()
+    used = np.zeros(kd.shape[:2], dtype=bool)
+    for r, L in enumerate(a["seq_lens"]):
+        for p in range(int(L)):
+            used[a["block_table"][r, p // 128], p % 128] = True
+    kd[~used] = np.uint16(0x7F00)  # bf16 1.7e38
+    a2 = dict(a, kdata=kd)
+    _same(_oracle_scores(a2, w.score_width), base)
+
+
+def test_page_permutation_invariance():
+    w = _small(7)
+    a = host_arrays(w)
+    base = _oracle_scores(a, w.score_width)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(a["kdata"].shape[0])  # new page p' holds old page perm[p']
+    inv = np.argsort(perm)
+    a2 = dict(a, kdata=a["kdata"][perm], block_table=inv[a["block_table"]].astype(np.int32))
+    _same(_oracle_scores(a2, w.score_width), base)
+
+
+def test_power_of_two_scale_is_exact():
+    w = _small(8)
+    a = host_arrays(w)
+    base = _oracle_scores(a, w.score_width)
+    a2 = dict(a, sm_scale=a["sm_scale"] * 4.0)
+    _same(_oracle_scores(a2, w.score_width), base * np.float32(4.0))
+
+
+def test_head_permutation_equivariance():
+    w = _small(9, H=3)
+    a = host_arrays(w)
+    base = _oracle_scores(a, w.score_width)
+    a2 = dict(a, q_bits=np.ascontiguousarray(a["q_bits"][:, ::-1]))
+    _same(_oracle_scores(a2, w.score_width), base[::-1])
+
+
+def test_rows_subset_matches_full():
+    w = _small(10)
+    a = host_arrays(w)
+    full = _oracle_scores(a, w.score_width)
+    rows = [0, 5, 7, 11]
+    sub = _oracle_scores(a, w.score_width, rows=rows)
+    _same(sub[:, rows], full[:, rows])
+    other = [t for t in range(w.rows) if t not in rows]
+    assert np.isnan(sub[:, other]).all()
+
+
+def test_short_requests_have_no_rows():
+    """seq_len < query_len: early rows sit before position 0 and see nothing."""
+    w = _small(12, R=2, lens=(2, 2), Q=4, H=1, fixed_lens=[2, 0])
+    a = host_arrays(w)
+    got = _oracle_scores(a, w.score_width)
+    assert np.isnan(got[0, [0, 1, 4, 5, 6, 7]]).all()
+    assert not np.isnan(got[0, [2, 3], 0]).any()
