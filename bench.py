@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark: block-scored paged index top-k on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: the decode scorer (paged-K gather + MFMA GEMV + causal block
+max) and the top-k selector, as one mm3_index_decode call (workloads 1, 2, 3,
+5), or mm3_index_score then mm3_index_topk (chunked prefill, workload 4).
+
+Default workload: the 64-request decode batch (seq_len ~ U[4096, 32768],
+query_len 4, 4 index heads, topk 16, 1 init + 2 local blocks).
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline      the dominant kernel (the scorer) against MI355X peak, from
+                HIP-event timing of that kernel alone inside this run;
+  cpu_baseline  the CPU oracle on this host, on a bounded sample;
+  selector      the top-k kernel's own timing.
+Inputs rotate between two copies of the page pool so that successive steps
+do not hit in the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "index-K tokens scored/s + top-k rows/s; % HBM peak (decode), % MFMA (prefill)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, datasheet
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--copies", type=int, default=2, help="page-pool copies rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU work for the oracle baseline")
+    return ap.parse_args()
+
+
+def algorithmic(w, seq):
+    """Algorithmic bytes (decode) and flops (prefill) of one pass."""
+    import numpy as np
+    Q, H, k = w.query_len, w.heads, w.topk
+    T = w.rows
+    t = np.arange(T)
+    pos = seq[t // Q].astype(np.int64) - Q + t % Q
+    nv = np.where(pos >= 0, pos // 128 + 1, 0)
+    key_b = w.key_bytes_per_token()
+    kbytes = int(seq.astype(np.int64).sum()) * key_b
+    qbytes = T * H * 256
+    tbytes = int(np.ceil(seq / 128).sum()) * 4
+    score_bytes = H * int(nv.sum()) * 4
+    out_bytes = H * T * k * 4
+    flops = 2 * 128 * H * int((pos + 1).clip(0).sum())
+    scorer = kbytes + qbytes + tbytes + score_bytes
+    return dict(k_bytes=kbytes, scorer_bytes=scorer,
+                step_bytes=kbytes + qbytes + tbytes + out_bytes,
+                selector_bytes=score_bytes + out_bytes, flops=flops,
+                tokens=int(seq.astype(np.int64).sum()), rows=H * T,
+                pairs=H * int((pos + 1).clip(0).sum()))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the indexer on one GPU; --gpus above 1 is not "
+              "supported (requests shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_block_paged_amd as mm3
+    from workloads import CONFIGS, config, host_subset
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cid = args.config
+    base = config(cid, device=dev)
+    seq = base.seq_lens.cpu().numpy()
+    copies = [base]
+    for _ in range(1, max(1, args.copies)):
+        import dataclasses
+        copies.append(dataclasses.replace(
+            base, kdata=base.kdata.clone(),
+            kscales=None if base.kscales is None else base.kscales.clone(),
+            q=base.q.clone(), block_table=base.block_table.clone(),
+            seq_lens=base.seq_lens.clone()))
+    prefill = base.heads * base.query_len > 16
+    H, T = base.heads, base.rows
+    outs = [torch.empty((H, T, base.topk), dtype=torch.int32, device=dev) for _ in copies]
+    scores = [torch.empty((H, T, base.score_width), dtype=torch.float32, device=dev) for _ in copies]
+    wss = []
+    for w in copies:
+        p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                             w.sm_scale, w.kscales)
+        n = mm3.decode_workspace_bytes(p, w.topk, False)
+        wss.append(torch.empty(max(n, 256), dtype=torch.uint8, device=dev))
+
+    def step(i):
+        c = i % len(copies)
+        w = copies[c]
+        if prefill:
+            mm3.mm3_index_score(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                w.max_seq_len, w.sm_scale, kscales=w.kscales, scores=scores[c])
+            mm3.mm3_index_topk(scores[c], w.seq_lens, w.query_len, w.max_seq_len, w.topk,
+                               w.init_blocks, w.local_blocks, out=outs[c])
+        else:
+            mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                 w.max_seq_len, w.sm_scale, w.topk, w.init_blocks,
+                                 w.local_blocks, kscales=w.kscales, out=outs[c],
+                                 workspace=wss[c])
+
+    def score_only(i):
+        c = i % len(copies)
+        w = copies[c]
+        mm3.mm3_index_score(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                            w.sm_scale, kscales=w.kscales, scores=scores[c])
+
+    def topk_only(i):
+        c = i % len(copies)
+        w = copies[c]
+        mm3.mm3_index_topk(scores[c], w.seq_lens, w.query_len, w.max_seq_len, w.topk,
+                           w.init_blocks, w.local_blocks, out=outs[c])
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms
+
+    # whole step (the contract's timed region)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # kernels alone, on the same stream (HIP events), same inputs
+    ms_score = timed(score_only, max(args.steps, 20), 3)
+    ms_topk = timed(topk_only, max(args.steps, 20), 3)
+
+    alg = algorithmic(base, seq)
+    tokens_per_s = alg["tokens"] / (ms * 1e-3)
+    rows_per_s = alg["rows"] / (ms * 1e-3)
+    if prefill:
+        achieved = alg["flops"] / (ms_score * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    traffic=None, kernel="prefill_score_kernel", ms=round(ms_score, 4),
+                    per_launch_flops=alg["flops"])
+    else:
+        achieved = alg["scorer_bytes"] / (ms_score * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="decode_score_kernel<%d>" % base.kfmt, ms=round(ms_score, 4),
+                    per_launch_bytes=alg["scorer_bytes"])
+    sel_gbs = alg["selector_bytes"] / (ms_topk * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(base, seq, args.cpu_seconds)
+
+    cfg = CONFIGS[cid]
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if base.kfmt == 0 else "nvfp4-keys/bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": base.name,
+            "num_reqs": base.num_reqs,
+            "seq_len_range": list(cfg["lens"]),
+            "sum_seq_len": alg["tokens"],
+            "query_len": base.query_len,
+            "index_heads": base.heads,
+            "head_dim": 128,
+            "block": 128,
+            "topk": base.topk,
+            "init_blocks": base.init_blocks,
+            "local_blocks": base.local_blocks,
+            "max_seq_len": base.max_seq_len,
+            "path": "score+topk" if prefill else "fused mm3_index_decode",
+            "pool_copies_rotated": len(copies),
+        },
+        "rows_per_s": round(rows_per_s, 1),
+        "roofline": roof,
+        "selector": dict(kernel="topk_kernel", ms=round(ms_topk, 4),
+                         achieved_gbs=round(sel_gbs, 1), bytes=alg["selector_bytes"]),
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, seq, seconds):
+    """The oracle as it is (single-threaded C, fp64) on this host, on whole
+    requests of the same workload, about `seconds` of work."""
+    import numpy as np
+
+    import oracle
+    from workloads import host_subset
+    order = list(range(w.num_reqs))
+    # estimate from the first request, then take as many as fit
+    done, tok, el = [], 0, 0.0
+    budget = seconds
+    for r in order:
+        a, rows = host_subset(w, [r])
+        rows_loc = None
+        if w.query_len > 64:  # prefill: a bounded sample of rows per request
+            rows_loc = list(range(0, w.query_len, max(1, w.query_len // 16)))
+        t0 = time.perf_counter()
+        oracle.forward(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
+                       a["seq_lens"], a["query_len"], a["sm_scale"], w.topk, w.init_blocks,
+                       w.local_blocks, w.score_width, rows=rows_loc)
+        el += time.perf_counter() - t0
+        nrows = w.query_len if rows_loc is None else len(rows_loc)
+        if w.query_len > 64:
+            tok += int(seq[r]) * nrows / w.query_len  # tokens-equivalent of sampled rows
+        else:
+            tok += int(seq[r])
+        done.append(r)
+        if el >= budget:
+            break
+    return {
+        "value": round(tok / el, 1),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {w.num_reqs} requests" +
+                   (" (every %d-th row)" % max(1, w.query_len // 16) if w.query_len > 64 else "") +
+                   f", {int(tok)} tokens, {el:.1f} s, single-threaded fp64 C oracle"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+if __name__ == "__main__":
+    main()

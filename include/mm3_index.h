@@ -1,0 +1,212 @@
+/*
+ * mm3_index.h -- C ABI of libmm3idx.so: block-scored, paged index top-k
+ * (the MiniMax-M3 lightning indexer) on AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Index queries q [tokens, heads, 128] (bf16) score every
+ * 128-token block of a paged index-K cache shared by all heads, one page per
+ * block, reached through an int32 block table and int32 sequence lengths.  A
+ * block's score is the maximum over its causally visible tokens of
+ * sm_scale * (q . k); each (head, token) row then selects its top-k block
+ * ids, with the leading "init" and trailing "local" blocks always kept and
+ * -1 padding.  Sources: page "vllm.models.minimax_m3.amd.ops.index_topk"
+ * (module docstring; minimax_m3_index_decode, minimax_m3_index_score and
+ * minimax_m3_index_topk docstrings and signatures), page
+ * "vllm.models.minimax_m3.amd.ops.indexer_context_parallel"
+ * (check_context_score_inputs: layout rules; indexer_context_scores:
+ * capture-stable max_seq_len and in-place out), page
+ * "vllm.models.minimax_m3.amd.indexer_nvfp4" (module docstring: NVFP4 keys
+ * score as e4m3_rn_satfinite(e2m1 * scale)).
+ *
+ * Conventions shared by every entry point
+ *  - Rows.  Request r owns rows t = r*query_len + j, j < query_len
+ *    (tokens == num_reqs * query_len, request-major).  Row t sits at
+ *    position pos = seq_lens[r] - query_len + j and sees the nv = pos/128 + 1
+ *    blocks b <= pos/128; in block b it sees tokens 128*b + s <= pos.  Rows
+ *    with pos < 0 see nothing.
+ *  - Pointers are DEVICE pointers unless a parameter says "host".  The
+ *    mm3_problem struct itself is read on the host during the call only.
+ *  - Strides are in ELEMENTS of the pointed-to type.
+ *  - stream is a hipStream_t (NULL = the legacy default stream).  All work is
+ *    enqueued asynchronously on it; nothing is read back to the host, no
+ *    device memory is allocated, and the grid depends only on host-side
+ *    arguments (never on device seq_lens), so every call can be captured in
+ *    a HIP graph and replayed with new device values.
+ *  - Ownership: the caller owns every buffer; the library keeps no pointer
+ *    after a call returns.
+ *  - Errors: every host-checkable rule is checked before anything is
+ *    enqueued; a non-zero return leaves every output untouched.
+ *    mm3_last_error() then describes it (thread-local).  Device VALUES are
+ *    preconditions, not checked: 0 <= seq_lens[r] <= max_seq_len and page
+ *    ids in [0, num_pages) for every visible block.
+ */
+#ifndef MM3_INDEX_H
+#define MM3_INDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define MM3_OK 0
+#define MM3_EINVAL (-1)       /* an argument breaks a rule listed below */
+#define MM3_EUNSUPPORTED (-2) /* valid, but not implemented by this build */
+#define MM3_EWORKSPACE (-3)   /* workspace NULL, misaligned or too small */
+#define MM3_EHIP (-4)         /* a HIP launch failed; message has the HIP error */
+
+/* index-K page formats */
+#define MM3_KFMT_BF16 0  /* kdata: bf16 [num_pages][128][128] */
+#define MM3_KFMT_NVFP4 1 /* kdata: u8 nibbles [num_pages][128][64], element 2i
+                            in the low nibble of byte i, 2i+1 in the high one;
+                            kscales: u8 e4m3 [num_pages][128][8], scale g
+                            covers d in [16g, 16g+16); key element =
+                            e4m3_rn_satfinite(e2m1(nibble) * e4m3(scale)) */
+
+#define MM3_BLOCK 128     /* tokens per sparse block == tokens per page */
+#define MM3_HEAD_DIM 128  /* index head dimension */
+#define MM3_MAX_BLOCKS 65534 /* cdiv(max_seq_len, 128) must stay below 65535 */
+#define MM3_MAX_TOPK 1024
+
+/*
+ * The scoring problem (page "ops.index_topk", minimax_m3_index_decode and
+ * minimax_m3_index_score signatures; page "indexer_context_parallel",
+ * check_context_score_inputs).
+ *   q            bf16, element (t, h, d) at q[t*q_tok_stride + h*q_head_stride + d];
+ *                D contiguous; 16-byte aligned; both strides multiples of 8.
+ *   heads        index heads H >= 1 (each head selects its own blocks).
+ *   kfmt/kdata/kscales/num_pages  the page pool (formats above), 16-byte
+ *                aligned, num_pages >= 1; kscales NULL for bf16.
+ *   block_table  int32, entry (r, b) at block_table[r*bt_row_stride + b];
+ *                bt_width >= cdiv(max_seq_len, 128); bt_row_stride >= bt_width.
+ *   seq_lens     int32 [num_reqs], contiguous.
+ *   query_len    rows per request, >= 1.
+ *   max_seq_len  capture-stable bound on every seq_lens[r] (e.g. the model's
+ *                maximum length, not the batch maximum); sizes the grids.
+ *   sm_scale     finite, > 0.
+ */
+typedef struct mm3_problem {
+    const void* q;
+    int64_t q_tok_stride;
+    int64_t q_head_stride;
+    int32_t heads;
+    int32_t kfmt;
+    const void* kdata;
+    const uint8_t* kscales;
+    int64_t num_pages;
+    const int32_t* block_table;
+    int64_t bt_row_stride;
+    int32_t bt_width;
+    const int32_t* seq_lens;
+    int32_t num_reqs;
+    int32_t query_len;
+    int32_t max_seq_len;
+    float sm_scale;
+} mm3_problem;
+
+/*
+ * mm3_index_score -- block scores (page "ops.index_topk",
+ * minimax_m3_index_score: "per-token index scores for each visible sparse
+ * block", each "the max over a 128-token index-K block").
+ *   scores  fp32, element (h, t, b) at scores[h*s_head_stride + t*s_row_stride + b],
+ *           s_width >= cdiv(max_seq_len,128) columns per row,
+ *           s_row_stride >= s_width, s_head_stride >= tokens*s_row_stride.
+ *           Written: every visible (h, t, b); nothing else is touched.
+ *   score = fl32(sm_scale * max over visible tokens of the fp32-accumulated
+ *           dot product of q[t, h, :] and the key).
+ * Rows with H*query_len <= 16 per request use the bandwidth-bound decode
+ * scorer; larger ones the MFMA prefill scorer.  NVFP4 keys: decode shapes only
+ * (MM3_EUNSUPPORTED otherwise).
+ */
+int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
+                    int64_t s_row_stride, int32_t s_width, void* stream);
+
+/*
+ * mm3_index_topk -- per (head, row) selection from a score tensor (page
+ * "ops.index_topk", minimax_m3_index_topk; forced blocks pinned as in page
+ * "indexer_cp_exchange", module docstring).
+ *   scores laid out as in mm3_index_score; only visible entries are read.
+ *   With F = [0, min(I,nv)) U [max(0,nv-L), nv):
+ *     nv <= topk -> ids 0..nv-1;  else F plus the topk-|F| best other blocks
+ *     by (score descending, id ascending; -0 == +0).
+ *   out int32, row (h, t) at out[h*o_head_stride + t*o_row_stride], written in
+ *   place: the selected ids ascending, then -1 up to topk.  Rows t >= tokens
+ *   are not touched (stable address for graph capture).
+ *   1 <= topk <= 1024, 0 <= I, 0 <= L, I + L <= topk,
+ *   o_row_stride >= topk, o_head_stride >= tokens*o_row_stride.
+ */
+int mm3_index_topk(const float* scores, int64_t s_head_stride,
+                   int64_t s_row_stride, int32_t s_width, int32_t heads,
+                   const int32_t* seq_lens, int32_t num_reqs, int32_t query_len,
+                   int32_t max_seq_len, int32_t topk, int32_t init_blocks,
+                   int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                   int64_t o_row_stride, void* stream);
+
+/*
+ * Workspace bytes mm3_index_decode needs for this problem when it is given
+ * no scores_out buffer (0 when scores_out is given).  Host-only, no HIP call.
+ * Returns 0 and sets mm3_last_error() if p is invalid.
+ */
+size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk,
+                                        int32_t with_scores_out);
+
+/*
+ * mm3_index_decode -- scores then top-k in one call (page "ops.index_topk",
+ * minimax_m3_index_decode: "decode index block-score followed by fused
+ * adaptive top-k selection", out written in place at a stable address).
+ *   out / topk / init_blocks / local_blocks as in mm3_index_topk.
+ *   scores_out  optional (NULL = keep scores in the workspace); when given it
+ *               receives the scores exactly as mm3_index_score writes them.
+ *   workspace   device memory of >= mm3_index_decode_workspace_bytes(),
+ *               256-byte aligned (NULL allowed when that is 0).  Its contents
+ *               need no initialisation; overlapping calls must not share it.
+ */
+int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
+                     int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                     int64_t o_row_stride, float* scores_out,
+                     int64_t s_head_stride, int64_t s_row_stride,
+                     int32_t s_width, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * mm3_build_sparse_block_table -- attention pages of the selected blocks, for
+ * ONE index head (page "ops.index_topk", minimax_m3_index_decode: the
+ * optional attention_block_table / sparse_block_table_out /
+ * sparse_context_lens_out / block_page_stride arguments).
+ *   topk_idx   int32 row t at topk_idx[t*o_row_stride], ids as mm3_index_topk
+ *              writes them (ascending, -1 padded).
+ *   attention_block_table  int32, request r's row at abt[r*abt_row_stride];
+ *              sparse block b owns entries [b*block_page_stride,
+ *              b*block_page_stride + pages_per_block);
+ *              abt_width >= cdiv(max_seq_len,128) * block_page_stride.
+ *   pages_per_block P >= 1; block_page_stride in {P, 2P}.
+ *   sparse_table int32, row t at sparse_table[t*st_row_stride], st_row_stride
+ *              >= topk*P: slot j*P+i = abt[r][b_j*stride + i] for the j-th id,
+ *              -1 for slots of -1 ids.
+ *   sparse_ctx_lens int32 [tokens]: sum over selected b of the visible tokens
+ *              of b, min(128, pos - 128*b + 1); 0 when pos < 0.
+ */
+int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride,
+                                 int32_t topk, const int32_t* seq_lens,
+                                 int32_t num_reqs, int32_t query_len,
+                                 int32_t max_seq_len,
+                                 const int32_t* attention_block_table,
+                                 int64_t abt_row_stride, int32_t abt_width,
+                                 int32_t pages_per_block,
+                                 int32_t block_page_stride,
+                                 int32_t* sparse_table, int64_t st_row_stride,
+                                 int32_t* sparse_ctx_lens, void* stream);
+
+/* Message for the last non-OK return on this thread ("" if none).  Host
+ * pointer, valid until the next call on this thread. */
+const char* mm3_last_error(void);
+
+/* Library version string (host pointer, static). */
+const char* mm3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MM3_INDEX_H */

@@ -1,0 +1,266 @@
+"""ctypes binding of libmm3idx.so (include/mm3_index.h).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+strides and the current HIP stream, and the C library does the rest.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback, so a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmm3idx.so")
+
+MM3_OK = 0
+MM3_EINVAL = -1
+MM3_EUNSUPPORTED = -2
+MM3_EWORKSPACE = -3
+MM3_EHIP = -4
+KFMT_BF16 = 0
+KFMT_NVFP4 = 1
+BLOCK = 128
+HEAD_DIM = 128
+
+EXPORTED = (
+    "mm3_index_score", "mm3_index_topk", "mm3_index_decode_workspace_bytes",
+    "mm3_index_decode", "mm3_build_sparse_block_table", "mm3_last_error",
+    "mm3_version",
+)
+
+
+class Mm3Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mm3 error {code}: {msg}")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("q_tok_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("heads", ctypes.c_int32),
+        ("kfmt", ctypes.c_int32),
+        ("kdata", ctypes.c_void_p),
+        ("kscales", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p),
+        ("bt_row_stride", ctypes.c_int64),
+        ("bt_width", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("num_reqs", ctypes.c_int32),
+        ("query_len", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(the HIP library is required; there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        PP = ctypes.POINTER(Problem)
+        L.mm3_index_score.argtypes = [PP, P, I64, I64, I32, P]
+        L.mm3_index_score.restype = ctypes.c_int
+        L.mm3_index_topk.argtypes = [P, I64, I64, I32, I32, P, I32, I32, I32, I32, I32, I32,
+                                     P, I64, I64, P]
+        L.mm3_index_topk.restype = ctypes.c_int
+        L.mm3_index_decode_workspace_bytes.argtypes = [PP, I32, I32]
+        L.mm3_index_decode_workspace_bytes.restype = SZ
+        L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, P]
+        L.mm3_index_decode.restype = ctypes.c_int
+        L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, P, I32, I32, I32, P, I64, I32,
+                                                   I32, I32, P, I64, P, P]
+        L.mm3_build_sparse_block_table.restype = ctypes.c_int
+        L.mm3_last_error.argtypes = []
+        L.mm3_last_error.restype = ctypes.c_char_p
+        L.mm3_version.argtypes = []
+        L.mm3_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != MM3_OK:
+        raise Mm3Error(rc, lib().mm3_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream=None):
+    if stream is not None:
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    if t.is_cuda:
+        return int(torch.cuda.current_stream(t.device).cuda_stream)
+    return None
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def score_width(max_seq_len: int) -> int:
+    """Default score row width: cdiv(max_seq_len, 128) rounded up to 16."""
+    return cdiv(cdiv(max_seq_len, BLOCK), 16) * 16
+
+
+def make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
+                 kscales=None) -> Problem:
+    """Marshal tensors into the C problem struct (no copies)."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != HEAD_DIM or q.stride(2) != 1:
+        raise ValueError("q must be bf16 [tokens, heads, 128] with contiguous D")
+    if kscales is None:
+        if kdata.dtype != torch.bfloat16 or tuple(kdata.shape[1:]) != (BLOCK, HEAD_DIM) \
+                or not kdata.is_contiguous():
+            raise ValueError("bf16 index cache must be contiguous [pages, 128, 128]")
+        kfmt = KFMT_BF16
+    else:
+        if kdata.dtype != torch.uint8 or tuple(kdata.shape[1:]) != (BLOCK, HEAD_DIM // 2) \
+                or not kdata.is_contiguous():
+            raise ValueError("NVFP4 nibbles must be contiguous uint8 [pages, 128, 64]")
+        if kscales.dtype != torch.uint8 or tuple(kscales.shape) != (kdata.shape[0], BLOCK, HEAD_DIM // 16) \
+                or not kscales.is_contiguous():
+            raise ValueError("NVFP4 scales must be contiguous uint8 [pages, 128, 8]")
+        kfmt = KFMT_NVFP4
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [reqs, width] with unit column stride")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [reqs]")
+    devs = {t.device for t in (q, kdata, block_table, seq_lens) + ((kscales,) if kscales is not None else ())}
+    if len(devs) != 1:
+        raise ValueError("all score inputs must be on the same device")
+    p = Problem()
+    p.q = q.data_ptr()
+    p.q_tok_stride = q.stride(0)
+    p.q_head_stride = q.stride(1)
+    p.heads = q.shape[1]
+    p.kfmt = kfmt
+    p.kdata = kdata.data_ptr()
+    p.kscales = _ptr(kscales)
+    p.num_pages = kdata.shape[0]
+    p.block_table = block_table.data_ptr()
+    p.bt_row_stride = block_table.stride(0)
+    p.bt_width = block_table.shape[1]
+    p.seq_lens = seq_lens.data_ptr()
+    p.num_reqs = seq_lens.shape[0]
+    p.query_len = int(query_len)
+    p.max_seq_len = int(max_seq_len)
+    p.sm_scale = float(sm_scale)
+    return p
+
+
+def mm3_index_score(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
+                    kscales=None, scores=None, stream=None):
+    """Block scores [heads, tokens, width] fp32 (only visible entries written)."""
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales)
+    if scores is None:
+        scores = torch.empty((q.shape[1], q.shape[0], score_width(max_seq_len)),
+                             dtype=torch.float32, device=q.device)
+    if scores.dtype != torch.float32 or scores.dim() != 3 or scores.stride(2) != 1:
+        raise ValueError("scores must be fp32 [heads, >=tokens, width] with unit column stride")
+    _check(lib().mm3_index_score(ctypes.byref(p), scores.data_ptr(), scores.stride(0),
+                                 scores.stride(1), scores.shape[2], _stream(q, stream)))
+    return scores
+
+
+def mm3_index_topk(scores, seq_lens, query_len, max_seq_len, topk, init_blocks, local_blocks,
+                   out=None, stream=None):
+    """Block ids [heads, tokens, topk] int32, written into out[:, :tokens] in place."""
+    H = scores.shape[0]
+    T = seq_lens.shape[0] * int(query_len)
+    if out is None:
+        out = torch.empty((H, T, topk), dtype=torch.int32, device=scores.device)
+    if scores.dtype != torch.float32 or scores.stride(2) != 1:
+        raise ValueError("scores must be fp32 with unit column stride")
+    if out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1 or out.shape[2] != topk \
+            or out.shape[0] != H or out.shape[1] < T:
+        raise ValueError("out must be int32 [heads, >=tokens, topk] with unit column stride")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32")
+    _check(lib().mm3_index_topk(scores.data_ptr(), scores.stride(0), scores.stride(1),
+                                scores.shape[2], H, seq_lens.data_ptr(), seq_lens.shape[0],
+                                int(query_len), int(max_seq_len), int(topk), int(init_blocks),
+                                int(local_blocks), out.data_ptr(), out.stride(0), out.stride(1),
+                                _stream(scores, stream)))
+    return out
+
+
+def decode_workspace_bytes(p: Problem, topk: int, with_scores_out: bool) -> int:
+    n = lib().mm3_index_decode_workspace_bytes(ctypes.byref(p), int(topk), int(with_scores_out))
+    err = lib().mm3_last_error().decode()
+    if n == 0 and err:
+        raise Mm3Error(MM3_EINVAL, err)
+    return n
+
+
+def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, topk,
+                     init_blocks, local_blocks, kscales=None, out=None, scores_out=None,
+                     workspace=None, stream=None):
+    """Scores then top-k in one call; returns out [heads, tokens, topk] int32."""
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales)
+    H, T = q.shape[1], q.shape[0]
+    if out is None:
+        out = torch.empty((H, T, topk), dtype=torch.int32, device=q.device)
+    if out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be int32 [heads, >=tokens, topk] with unit column stride")
+    need = decode_workspace_bytes(p, topk, scores_out is not None)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scores_out is not None:
+        if scores_out.dtype != torch.float32 or scores_out.stride(2) != 1:
+            raise ValueError("scores_out must be fp32 with unit column stride")
+        sh, sr, sw = scores_out.stride(0), scores_out.stride(1), scores_out.shape[2]
+    else:
+        sh = sr = sw = 0
+    _check(lib().mm3_index_decode(ctypes.byref(p), int(topk), int(init_blocks), int(local_blocks),
+                                  out.data_ptr(), out.stride(0), out.stride(1), _ptr(scores_out),
+                                  sh, sr, sw, ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def mm3_build_sparse_block_table(topk_idx, seq_lens, query_len, max_seq_len,
+                                 attention_block_table, pages_per_block, block_page_stride,
+                                 sparse_table=None, sparse_ctx_lens=None, stream=None):
+    """(sparse_table [tokens, topk*P], sparse_ctx_lens [tokens]) for one head."""
+    if topk_idx.dim() == 3:
+        if topk_idx.shape[0] != 1:
+            raise ValueError("the sparse table is built for one index head")
+        topk_idx = topk_idx[0]
+    T, K = topk_idx.shape[0], topk_idx.shape[1]
+    P = int(pages_per_block)
+    if sparse_table is None:
+        sparse_table = torch.empty((T, K * P), dtype=torch.int32, device=topk_idx.device)
+    if sparse_ctx_lens is None:
+        sparse_ctx_lens = torch.empty((T,), dtype=torch.int32, device=topk_idx.device)
+    for t in (topk_idx, attention_block_table, sparse_table, sparse_ctx_lens, seq_lens):
+        if t.dtype != torch.int32 or t.stride(-1) != 1:
+            raise ValueError("sparse-table tensors must be int32 with contiguous rows")
+    _check(lib().mm3_build_sparse_block_table(
+        topk_idx.data_ptr(), topk_idx.stride(0), K, seq_lens.data_ptr(), seq_lens.shape[0],
+        int(query_len), int(max_seq_len), attention_block_table.data_ptr(),
+        attention_block_table.stride(0), attention_block_table.shape[1], P,
+        int(block_page_stride), sparse_table.data_ptr(), sparse_table.stride(0),
+        sparse_ctx_lens.data_ptr(), _stream(topk_idx, stream)))
+    return sparse_table, sparse_ctx_lens
+
+
+def version() -> str:
+    return lib().mm3_version().decode()

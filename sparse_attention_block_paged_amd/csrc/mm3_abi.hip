@@ -1,0 +1,322 @@
+// mm3_abi.hip -- the C ABI declared in include/mm3_index.h: host-side
+// validation, launch policy and kernel launches.  No device memory is
+// allocated or read here, and grids depend only on host arguments, so every
+// entry point can be captured in a HIP graph.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "mm3_index.h"
+#include "mm3_launch.h"
+
+using namespace mm3;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MM3_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MM3_EHIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Rules every scorer entry point shares (page "indexer_context_parallel",
+// check_context_score_inputs and indexer_context_scores; page
+// "ops.index_topk", minimax_m3_index_decode).
+int check_problem(const mm3_problem* p) {
+  if (!p) return fail(MM3_EINVAL, "problem is NULL");
+  if (p->heads < 1) return fail(MM3_EINVAL, "heads must be >= 1, got %d", p->heads);
+  if (p->query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1, got %d", p->query_len);
+  if (p->num_reqs < 0) return fail(MM3_EINVAL, "num_reqs must be >= 0, got %d", p->num_reqs);
+  if (p->max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
+  const int64_t nb = cdiv64(p->max_seq_len, MM3_BLOCK);
+  if (nb > MM3_MAX_BLOCKS)
+    return fail(MM3_EINVAL, "cdiv(max_seq_len,128) = %lld must be below 65535", (long long)nb);
+  if (!(isfinite(p->sm_scale) && p->sm_scale > 0.0f))
+    return fail(MM3_EINVAL, "sm_scale must be finite and > 0");
+  if (p->kfmt != MM3_KFMT_BF16 && p->kfmt != MM3_KFMT_NVFP4)
+    return fail(MM3_EINVAL, "unknown index-K format %d", p->kfmt);
+  if (p->num_pages < 1) return fail(MM3_EINVAL, "index cache must hold >= 1 page");
+  if (!p->q || !p->kdata || !p->block_table || !p->seq_lens)
+    return fail(MM3_EINVAL, "q, kdata, block_table and seq_lens must be non-NULL");
+  if (p->kfmt == MM3_KFMT_NVFP4 && !p->kscales)
+    return fail(MM3_EINVAL, "NVFP4 index cache needs kscales");
+  if (!aligned(p->q, 16) || !aligned(p->kdata, 16) || (p->kscales && !aligned(p->kscales, 2)))
+    return fail(MM3_EINVAL, "q and kdata must be 16-byte aligned, kscales 2-byte aligned");
+  if (p->q_tok_stride % 8 || p->q_head_stride % 8 || p->q_tok_stride < 0 || p->q_head_stride < 0)
+    return fail(MM3_EINVAL, "q strides must be non-negative multiples of 8 elements");
+  if (p->heads > 1 && p->q_head_stride < MM3_HEAD_DIM)
+    return fail(MM3_EINVAL, "q head stride must be >= 128 (D contiguous, heads disjoint)");
+  if (p->bt_width < nb)
+    return fail(MM3_EINVAL, "block table width %d narrower than cdiv(max_seq_len,128) = %lld",
+                p->bt_width, (long long)nb);
+  if (p->num_reqs > 1 && p->bt_row_stride < p->bt_width)
+    return fail(MM3_EINVAL, "block table row stride must be >= its width");
+  return MM3_OK;
+}
+
+int check_scores(const mm3_problem* p, const float* s, int64_t sh, int64_t sr, int32_t sw) {
+  const int64_t T = (int64_t)p->num_reqs * p->query_len;
+  const int64_t nb = cdiv64(p->max_seq_len, MM3_BLOCK);
+  if (!s) return fail(MM3_EINVAL, "scores must be non-NULL");
+  if (!aligned(s, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
+  if (sw < nb) return fail(MM3_EINVAL, "score width %d < cdiv(max_seq_len,128) = %lld", sw, (long long)nb);
+  if (T > 1 && sr < sw) return fail(MM3_EINVAL, "score row stride must be >= score width");
+  if (p->heads > 1 && sh < T * sr) return fail(MM3_EINVAL, "score head stride must be >= tokens * row stride");
+  if (sh < 0 || sr < 0) return fail(MM3_EINVAL, "score strides must be non-negative");
+  return MM3_OK;
+}
+
+int check_select(int32_t topk, int32_t I, int32_t L) {
+  if (topk < 1 || topk > MM3_MAX_TOPK) return fail(MM3_EINVAL, "topk must be in [1, 1024], got %d", topk);
+  if (I < 0 || L < 0) return fail(MM3_EINVAL, "init_blocks and local_blocks must be >= 0");
+  if ((int64_t)I + L > topk)
+    return fail(MM3_EINVAL, "init_blocks + local_blocks (%d) exceeds topk (%d)", I + L, topk);
+  return MM3_OK;
+}
+
+int check_out(int32_t* out, int64_t oh, int64_t orow, int32_t heads, int64_t T, int32_t topk) {
+  if (!out) return fail(MM3_EINVAL, "out must be non-NULL");
+  if (!aligned(out, 4)) return fail(MM3_EINVAL, "out must be 4-byte aligned");
+  if (oh < 0 || orow < 0) return fail(MM3_EINVAL, "out strides must be non-negative");
+  if (T > 1 && orow < topk) return fail(MM3_EINVAL, "out row stride must be >= topk");
+  if (heads > 1 && oh < T * orow) return fail(MM3_EINVAL, "out head stride must be >= tokens * row stride");
+  return MM3_OK;
+}
+
+ScoreArgs score_args(const mm3_problem* p, float* s, int64_t sh, int64_t sr) {
+  ScoreArgs a{};
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.q_tok = p->q_tok_stride;
+  a.q_head = p->q_head_stride;
+  a.kdata = static_cast<const uint8_t*>(p->kdata);
+  a.kscales = p->kscales;
+  a.bt = p->block_table;
+  a.bt_stride = p->bt_row_stride;
+  a.seq_lens = p->seq_lens;
+  a.scores = s;
+  a.s_head = sh;
+  a.s_row = sr;
+  a.heads = p->heads;
+  a.qlen = p->query_len;
+  a.num_reqs = p->num_reqs;
+  a.nb_max = (int32_t)cdiv64(p->max_seq_len, MM3_BLOCK);
+  a.sm_scale = p->sm_scale;
+  // Decode: each wave scores a few pages; aim for enough workgroups to
+  // cover the chip several times at the capture-stable size.
+  const int64_t total = (int64_t)p->num_reqs * a.nb_max;
+  int bpw = 4;  // blocks per workgroup (4 waves)
+  while (bpw < 32 && total / bpw > 8192) bpw *= 2;
+  a.blocks_per_wg = bpw;
+  return a;
+}
+
+bool is_decode_shape(const mm3_problem* p) {
+  return (int64_t)p->heads * p->query_len <= kDecodeRows;
+}
+
+int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStream_t st) {
+  const ScoreArgs a = score_args(p, s, sh, sr);
+  hipError_t e;
+  if (is_decode_shape(p))
+    e = p->kfmt == MM3_KFMT_BF16 ? launch_decode_score_bf16(a, st) : launch_decode_score_nvfp4(a, st);
+  else
+    e = launch_prefill_score_bf16(a, st);
+  return e == hipSuccess ? MM3_OK : hip_fail(e, "scorer launch");
+}
+
+int check_shape_supported(const mm3_problem* p) {
+  if (!is_decode_shape(p) && p->kfmt != MM3_KFMT_BF16)
+    return fail(MM3_EUNSUPPORTED, "NVFP4 keys are scored for heads*query_len <= 16 only");
+  return MM3_OK;
+}
+
+TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t heads, const int32_t* seq,
+                   int32_t R, int32_t Q, int32_t max_seq_len, int32_t topk, int32_t I, int32_t L,
+                   int32_t* out, int64_t oh, int64_t orow) {
+  TopkArgs a{};
+  a.scores = s;
+  a.s_head = sh;
+  a.s_row = sr;
+  a.seq_lens = seq;
+  a.out = out;
+  a.o_head = oh;
+  a.o_row = orow;
+  a.heads = heads;
+  a.qlen = Q;
+  a.num_reqs = R;
+  a.topk = topk;
+  a.init_blocks = I;
+  a.local_blocks = L;
+  a.nb_max = (int32_t)cdiv64(max_seq_len, MM3_BLOCK);
+  return a;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mm3_last_error(void) { return g_err.c_str(); }
+
+const char* mm3_version(void) { return "mm3idx 0.1 gfx950"; }
+
+int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
+                    int64_t s_row_stride, int32_t s_width, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_scores(p, scores, s_head_stride, s_row_stride, s_width))) return rc;
+  if ((rc = check_shape_supported(p))) return rc;
+  if ((int64_t)p->num_reqs * p->query_len == 0 || p->max_seq_len == 0) return ok();
+  if ((rc = launch_scores(p, scores, s_head_stride, s_row_stride, (hipStream_t)stream))) return rc;
+  return ok();
+}
+
+int mm3_index_topk(const float* scores, int64_t s_head_stride, int64_t s_row_stride,
+                   int32_t s_width, int32_t heads, const int32_t* seq_lens, int32_t num_reqs,
+                   int32_t query_len, int32_t max_seq_len, int32_t topk, int32_t init_blocks,
+                   int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                   int64_t o_row_stride, void* stream) {
+  if (heads < 1) return fail(MM3_EINVAL, "heads must be >= 1");
+  if (query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1");
+  if (num_reqs < 0 || max_seq_len < 0) return fail(MM3_EINVAL, "num_reqs and max_seq_len must be >= 0");
+  const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
+  if (nb > MM3_MAX_BLOCKS) return fail(MM3_EINVAL, "cdiv(max_seq_len,128) must be below 65535");
+  int rc = check_select(topk, init_blocks, local_blocks);
+  if (rc) return rc;
+  const int64_t T = (int64_t)num_reqs * query_len;
+  if (!seq_lens) return fail(MM3_EINVAL, "seq_lens must be non-NULL");
+  if (!scores) return fail(MM3_EINVAL, "scores must be non-NULL");
+  if (!aligned(scores, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
+  if (s_width < nb) return fail(MM3_EINVAL, "score width < cdiv(max_seq_len,128)");
+  if (s_head_stride < 0 || s_row_stride < 0) return fail(MM3_EINVAL, "score strides must be non-negative");
+  if (T > 1 && s_row_stride < s_width) return fail(MM3_EINVAL, "score row stride must be >= score width");
+  if (heads > 1 && s_head_stride < T * s_row_stride)
+    return fail(MM3_EINVAL, "score head stride must be >= tokens * row stride");
+  if ((rc = check_out(out, o_head_stride, o_row_stride, heads, T, topk))) return rc;
+  if (T == 0) return ok();
+  TopkArgs a = topk_args(scores, s_head_stride, s_row_stride, heads, seq_lens, num_reqs, query_len,
+                         max_seq_len, topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride);
+  hipError_t e = launch_topk(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk, int32_t with_scores_out) {
+  if (check_problem(p)) return 0;
+  if (check_select(topk, 0, 0)) return 0;
+  g_err.clear();
+  if (with_scores_out) return 0;
+  const int64_t T = (int64_t)p->num_reqs * p->query_len;
+  const int64_t width = cdiv64(cdiv64(p->max_seq_len, MM3_BLOCK), 16) * 16;
+  return round256((size_t)(p->heads * T * width) * sizeof(float));
+}
+
+int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
+                     int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                     int64_t o_row_stride, float* scores_out, int64_t s_head_stride,
+                     int64_t s_row_stride, int32_t s_width, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
+  const int64_t T = (int64_t)p->num_reqs * p->query_len;
+  if ((rc = check_out(out, o_head_stride, o_row_stride, p->heads, T, topk))) return rc;
+  if ((rc = check_shape_supported(p))) return rc;
+  float* s = scores_out;
+  int64_t sh = s_head_stride, sr = s_row_stride;
+  int32_t sw = s_width;
+  if (s) {
+    if ((rc = check_scores(p, s, sh, sr, sw))) return rc;
+  } else {
+    const size_t need = mm3_index_decode_workspace_bytes(p, topk, 0);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+      return fail(MM3_EWORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes (got %zu)",
+                  need, workspace_bytes);
+    sw = (int32_t)(cdiv64(cdiv64(p->max_seq_len, MM3_BLOCK), 16) * 16);
+    sr = sw;
+    sh = T * sr;
+    s = static_cast<float*>(workspace);
+  }
+  if (T == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  if (p->max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
+  TopkArgs a = topk_args(s, sh, sr, p->heads, p->seq_lens, p->num_reqs, p->query_len, p->max_seq_len,
+                         topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride);
+  hipError_t e = launch_topk(a, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, int32_t topk,
+                                 const int32_t* seq_lens, int32_t num_reqs, int32_t query_len,
+                                 int32_t max_seq_len, const int32_t* attention_block_table,
+                                 int64_t abt_row_stride, int32_t abt_width,
+                                 int32_t pages_per_block, int32_t block_page_stride,
+                                 int32_t* sparse_table, int64_t st_row_stride,
+                                 int32_t* sparse_ctx_lens, void* stream) {
+  if (!topk_idx || !seq_lens || !attention_block_table || !sparse_table || !sparse_ctx_lens)
+    return fail(MM3_EINVAL, "sparse-table arguments must be provided together (non-NULL)");
+  if (topk < 1 || topk > MM3_MAX_TOPK) return fail(MM3_EINVAL, "topk must be in [1, 1024]");
+  if (query_len < 1 || num_reqs < 0 || max_seq_len < 0)
+    return fail(MM3_EINVAL, "query_len >= 1, num_reqs >= 0, max_seq_len >= 0 required");
+  const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
+  if (nb > MM3_MAX_BLOCKS) return fail(MM3_EINVAL, "cdiv(max_seq_len,128) must be below 65535");
+  if (pages_per_block < 1) return fail(MM3_EINVAL, "pages_per_block must be >= 1");
+  if (block_page_stride != pages_per_block && block_page_stride != 2 * pages_per_block)
+    return fail(MM3_EINVAL, "block_page_stride must be P or 2P (P=%d), got %d", pages_per_block,
+                block_page_stride);
+  if ((int64_t)abt_width < nb * block_page_stride)
+    return fail(MM3_EINVAL, "attention block table narrower than cdiv(max_seq_len,128)*stride");
+  if (num_reqs > 1 && abt_row_stride < abt_width)
+    return fail(MM3_EINVAL, "attention block table row stride must be >= its width");
+  const int64_t T = (int64_t)num_reqs * query_len;
+  if (T > 1 && o_row_stride < topk) return fail(MM3_EINVAL, "topk row stride must be >= topk");
+  if (T > 1 && st_row_stride < (int64_t)topk * pages_per_block)
+    return fail(MM3_EINVAL, "sparse table row stride must be >= topk * pages_per_block");
+  if (!aligned(topk_idx, 4) || !aligned(sparse_table, 4) || !aligned(sparse_ctx_lens, 4) ||
+      !aligned(attention_block_table, 4))
+    return fail(MM3_EINVAL, "int32 buffers must be 4-byte aligned");
+  if (T == 0) return ok();
+  SparseTableArgs a{};
+  a.topk_idx = topk_idx;
+  a.o_row = o_row_stride;
+  a.seq_lens = seq_lens;
+  a.abt = attention_block_table;
+  a.abt_row = abt_row_stride;
+  a.sparse = sparse_table;
+  a.st_row = st_row_stride;
+  a.ctx_lens = sparse_ctx_lens;
+  a.topk = topk;
+  a.qlen = query_len;
+  a.num_reqs = num_reqs;
+  a.pages_per_block = pages_per_block;
+  a.block_page_stride = block_page_stride;
+  hipError_t e = launch_sparse_table(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse-table launch");
+  return ok();
+}
+
+}  // extern "C"

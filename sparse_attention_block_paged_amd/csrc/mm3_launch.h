@@ -1,0 +1,77 @@
+// mm3_launch.h -- internal kernel argument blocks and launchers.  The C ABI
+// (mm3_abi.cpp) validates every host-visible rule before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm3 {
+
+// Everything a scorer reads.  Strides in elements.
+struct ScoreArgs {
+  const uint16_t* q;        // bf16 bits [T, H, 128]
+  int64_t q_tok;
+  int64_t q_head;
+  const uint8_t* kdata;     // bf16 [P,128,128] or nvfp4 nibbles [P,128,64]
+  const uint8_t* kscales;   // nvfp4 e4m3 scales [P,128,8]
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+  float* scores;            // [H, T, >=nb] fp32
+  int64_t s_head;
+  int64_t s_row;
+  int32_t heads;
+  int32_t qlen;
+  int32_t num_reqs;
+  int32_t nb_max;           // cdiv(max_seq_len, 128)
+  int32_t blocks_per_wg;    // decode: blocks one workgroup covers
+  int32_t nsplit;           // prefill: block splits per row tile
+  float sm_scale;
+};
+
+struct TopkArgs {
+  const float* scores;
+  int64_t s_head;
+  int64_t s_row;
+  const int32_t* seq_lens;
+  int32_t* out;
+  int64_t o_head;
+  int64_t o_row;
+  int32_t heads;
+  int32_t qlen;
+  int32_t num_reqs;
+  int32_t topk;
+  int32_t init_blocks;
+  int32_t local_blocks;
+  int32_t nb_max;
+};
+
+struct SparseTableArgs {
+  const int32_t* topk_idx;
+  int64_t o_row;
+  const int32_t* seq_lens;
+  const int32_t* abt;
+  int64_t abt_row;
+  int32_t* sparse;
+  int64_t st_row;
+  int32_t* ctx_lens;
+  int32_t topk;
+  int32_t qlen;
+  int32_t num_reqs;
+  int32_t pages_per_block;
+  int32_t block_page_stride;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s);
+
+// Rows one decode-scorer MFMA tile holds (heads * query_len must fit).
+constexpr int kDecodeRows = 16;
+// Flattened (token, head) rows of one prefill workgroup tile.
+constexpr int kPrefillRows = 256;
+
+}  // namespace mm3

@@ -1,0 +1,171 @@
+// topk.hip -- per (head, row) block selection and the sparse block table.
+//
+// What it computes (page "vllm.models.minimax_m3.amd.ops.index_topk", module
+// docstring and minimax_m3_index_topk / minimax_m3_index_decode docstrings;
+// page "indexer_cp_exchange", module docstring, for the pinned forced
+// blocks): each (head, row) keeps the init and local blocks and fills the
+// rest of its topk slots with the best-scoring other visible blocks,
+// 0-indexed, -1 padded.  Ties go to the lower block id; ids are written in
+// ascending order.
+//
+// Design.  One wavefront per row.  Each lane holds the scores of blocks
+// lane, lane+64, ... as order-preserving u32 keys (forced blocks get the
+// largest key), so the k-th largest key T is found by a 32-step bitwise
+// search whose counts are wave ballots + scalar popcounts.  Blocks with
+// key > T are taken, and keys == T are taken in ascending id order until
+// topk are chosen; the same ballot prefix counts (mbcnt) give each chosen id
+// its output slot, so the row is written already sorted.  This replaces the
+// pages' packed 64-bit (score, id) keys and partial-top-k merges with a
+// single-pass threshold select that needs no workspace.
+#include "mm3_device.h"
+#include "mm3_launch.h"
+
+namespace mm3 {
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+__device__ __forceinline__ uint32_t block_key(const float* srow, int b, int nv, int I, int L) {
+  if (b >= nv) return 0u;  // not a candidate (every finite score maps above 0)
+  if (b < I || b >= nv - L) return kForcedKey;
+  return order_key(srow[b]);
+}
+
+// E keys per lane in registers: rows with nv <= 64*E.
+template <int E>
+__device__ void select_regs(const float* srow, int nv, const TopkArgs& a, int32_t* orow, int lane) {
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = block_key(srow, 64 * e + lane, nv, a.init_blocks, a.local_blocks);
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+    if (cnt >= a.topk) T = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
+  const int need = a.topk - gt;
+  int base = 0, tie_base = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t tmask = __ballot(key[e] == T);
+    const bool sel = key[e] > T || (key[e] == T && tie_base + lanes_below(tmask) < need);
+    const uint64_t smask = __ballot(sel);
+    if (sel) orow[base + lanes_below(smask)] = 64 * e + lane;
+    base += __popcll(smask);
+    tie_base += __popcll(tmask);
+  }
+}
+
+// Any nv: keys re-read from the score row on every pass.
+__device__ void select_generic(const float* srow, int nv, const TopkArgs& a, int32_t* orow, int lane) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
+    for (int b0 = 0; b0 < nv; b0 += 64)
+      cnt += __popcll(__ballot(block_key(srow, b0 + lane, nv, a.init_blocks, a.local_blocks) >= cand));
+    if (cnt >= a.topk) T = cand;
+  }
+  int gt = 0;
+  for (int b0 = 0; b0 < nv; b0 += 64)
+    gt += __popcll(__ballot(block_key(srow, b0 + lane, nv, a.init_blocks, a.local_blocks) > T));
+  const int need = a.topk - gt;
+  int base = 0, tie_base = 0;
+  for (int b0 = 0; b0 < nv; b0 += 64) {
+    const uint32_t k = block_key(srow, b0 + lane, nv, a.init_blocks, a.local_blocks);
+    const uint64_t tmask = __ballot(k == T);
+    const bool sel = k > T || (k == T && tie_base + lanes_below(tmask) < need);
+    const uint64_t smask = __ballot(sel);
+    if (sel) orow[base + lanes_below(smask)] = b0 + lane;
+    base += __popcll(smask);
+    tie_base += __popcll(tmask);
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = a.num_reqs * a.qlen;
+  const int t = blockIdx.x * 4 + wave;
+  const int h = blockIdx.y;
+  if (t >= T) return;
+  const int r = t / a.qlen, j = t - r * a.qlen;
+  const int pos = a.seq_lens[r] - a.qlen + j;
+  int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)t * a.o_row;
+  const int nv = pos < 0 ? 0 : pos / kBlock + 1;
+  if (nv <= a.topk) {
+    for (int k = lane; k < a.topk; k += 64) orow[k] = k < nv ? k : -1;
+    return;
+  }
+  const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
+  if (E > 0)
+    select_regs<(E > 0 ? E : 1)>(srow, nv, a, orow, lane);
+  else
+    select_generic(srow, nv, a, orow, lane);
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  const int T = a.num_reqs * a.qlen;
+  dim3 grid((T + 3) / 4, a.heads), block(256);
+  const int nb = a.nb_max;
+  if (nb <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, a);
+  else if (nb <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, a);
+  else if (nb <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
+  else if (nb <= 512)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
+  else if (nb <= 1024)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<0>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ sparse block table
+//
+// For one index head (page "ops.index_topk", minimax_m3_index_decode, the
+// optional sparse-table arguments): the P attention pages of each selected
+// block, and the number of tokens the row's sparse context holds.  One wave
+// per row; lanes walk the topk*P output slots.
+
+__global__ __launch_bounds__(256) void sparse_table_kernel(SparseTableArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = a.num_reqs * a.qlen;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int r = t / a.qlen, j = t - r * a.qlen;
+  const int pos = a.seq_lens[r] - a.qlen + j;
+  const int32_t* ids = a.topk_idx + (int64_t)t * a.o_row;
+  const int32_t* abt = a.abt + (int64_t)r * a.abt_row;
+  int32_t* st = a.sparse + (int64_t)t * a.st_row;
+  const int P = a.pages_per_block, slots = a.topk * P;
+  for (int x = lane; x < slots; x += 64) {
+    const int k = x / P, i = x - k * P;
+    const int b = ids[k];
+    st[x] = b < 0 ? -1 : abt[(int64_t)b * a.block_page_stride + i];
+  }
+  int len = 0;
+  for (int k = lane; k < a.topk; k += 64) {
+    const int b = ids[k];
+    if (b >= 0 && pos >= 0) len += max(0, min(kBlock, pos - kBlock * b + 1));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) len += __shfl_xor(len, off, 64);
+  if (lane == 0) a.ctx_lens[t] = len;
+}
+
+hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s) {
+  const int T = a.num_reqs * a.qlen;
+  hipLaunchKernelGGL(sparse_table_kernel, dim3((T + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mm3

@@ -1,0 +1,219 @@
+"""The C ABI without a GPU: exports, struct layout, host-side validation.
+
+Validation happens before anything is enqueued, so these calls use fake
+(never dereferenced) device pointers and run on a machine with no GPU.  Each
+rejected call must return its documented code and describe the problem.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_block_paged_amd as mm3
+from sparse_attention_block_paged_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mm3_index.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(mm3_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 7
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTED)
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, re.M), f"{n} not a defined text symbol"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in B.Problem._fields_]
+    body = "".join(f'printf("%zu ", offsetof(mm3_problem, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mm3_index.h"\n'
+                   f'int main(void){{ {body} printf("%zu\\n", sizeof(mm3_problem)); return 0; }}\n')
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [getattr(B.Problem, f).offset for f in fields] + [ctypes.sizeof(B.Problem)]
+    assert got == want
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+
+
+def _problem(**kw):
+    p = B.Problem()
+    d = dict(q=FAKE, q_tok_stride=4 * 128, q_head_stride=128, heads=4, kfmt=0, kdata=FAKE * 2,
+             kscales=None, num_pages=100, block_table=FAKE * 3, bt_row_stride=64, bt_width=64,
+             seq_lens=FAKE * 4, num_reqs=8, query_len=4, max_seq_len=8192, sm_scale=0.088)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def _score(p, sh=None, sr=64, sw=64, scores=FAKE * 5):
+    T = p.num_reqs * p.query_len
+    sh = T * sr if sh is None else sh
+    return B.lib().mm3_index_score(ctypes.byref(p), scores, sh, sr, sw, None)
+
+
+def _err():
+    return B.lib().mm3_last_error().decode()
+
+
+BAD_PROBLEMS = [
+    ("heads", dict(heads=0), "heads"),
+    ("query_len", dict(query_len=0), "query_len"),
+    ("num_reqs", dict(num_reqs=-1), "num_reqs"),
+    ("max_seq_len", dict(max_seq_len=-5), "max_seq_len"),
+    ("too_many_blocks", dict(max_seq_len=65535 * 128, bt_width=70000, bt_row_stride=70000), "65535"),
+    ("sm_scale_zero", dict(sm_scale=0.0), "sm_scale"),
+    ("sm_scale_neg", dict(sm_scale=-1.0), "sm_scale"),
+    ("sm_scale_nan", dict(sm_scale=float("nan")), "sm_scale"),
+    ("sm_scale_inf", dict(sm_scale=float("inf")), "sm_scale"),
+    ("kfmt", dict(kfmt=7), "format"),
+    ("no_pages", dict(num_pages=0), "page"),
+    ("null_q", dict(q=None), "non-NULL"),
+    ("null_table", dict(block_table=None), "non-NULL"),
+    ("null_lens", dict(seq_lens=None), "non-NULL"),
+    ("nvfp4_no_scales", dict(kfmt=1), "kscales"),
+    ("q_misaligned", dict(q=FAKE + 8), "aligned"),
+    ("k_misaligned", dict(kdata=FAKE * 2 + 4), "aligned"),
+    ("q_stride", dict(q_tok_stride=4 * 128 + 4), "multiples of 8"),
+    ("q_head_overlap", dict(q_head_stride=64), "head stride"),
+    ("table_narrow", dict(bt_width=63), "narrower"),
+    ("table_row_stride", dict(bt_row_stride=32), "row stride"),
+]
+
+
+@pytest.mark.parametrize("label,kw,msg", BAD_PROBLEMS, ids=[b[0] for b in BAD_PROBLEMS])
+def test_problem_rules(label, kw, msg):
+    p = _problem(**kw)
+    assert _score(p) == B.MM3_EINVAL
+    assert msg in _err(), _err()
+    # the same rule guards the fused entry point
+    rc = B.lib().mm3_index_decode(ctypes.byref(p), 16, 1, 2, FAKE * 6, 32 * 16, 16, None, 0, 0, 0,
+                                  FAKE * 7, 1 << 30, None)
+    assert rc == B.MM3_EINVAL
+
+
+BAD_SCORES = [
+    ("null", dict(scores=None), "non-NULL"),
+    ("misaligned", dict(scores=FAKE * 5 + 2), "aligned"),
+    ("narrow", dict(sw=63), "score width"),
+    ("row_stride", dict(sr=32, sw=64), "row stride"),
+    ("head_stride", dict(sh=10), "head stride"),
+]
+
+
+@pytest.mark.parametrize("label,kw,msg", BAD_SCORES, ids=[b[0] for b in BAD_SCORES])
+def test_score_buffer_rules(label, kw, msg):
+    assert _score(_problem(), **kw) == B.MM3_EINVAL
+    assert msg in _err(), _err()
+
+
+def test_nvfp4_prefill_shape_unsupported():
+    p = _problem(kfmt=1, kscales=FAKE * 8, query_len=64)
+    assert _score(p) == B.MM3_EUNSUPPORTED
+    assert "NVFP4" in _err()
+
+
+def test_empty_batch_returns_ok_without_launch():
+    assert _score(_problem(num_reqs=0)) == B.MM3_OK
+    assert _err() == ""
+    rc = B.lib().mm3_index_topk(FAKE, 0, 64, 64, 4, FAKE * 4, 0, 4, 8192, 16, 1, 2, FAKE * 6, 0,
+                                16, None)
+    assert rc == B.MM3_OK
+
+
+def _topk(**kw):
+    d = dict(scores=FAKE, sh=32 * 64, sr=64, sw=64, heads=4, seq=FAKE * 4, R=8, Q=4, msl=8192,
+             topk=16, I=1, L=2, out=FAKE * 6, oh=32 * 16, orow=16)
+    d.update(kw)
+    return B.lib().mm3_index_topk(d["scores"], d["sh"], d["sr"], d["sw"], d["heads"], d["seq"],
+                                  d["R"], d["Q"], d["msl"], d["topk"], d["I"], d["L"], d["out"],
+                                  d["oh"], d["orow"], None)
+
+
+BAD_TOPK = [
+    ("topk_zero", dict(topk=0), "topk"),
+    ("topk_big", dict(topk=1025, orow=1025, oh=32 * 1025), "topk"),
+    ("forced_exceed", dict(topk=4, I=3, L=2, orow=4, oh=128), "exceeds"),
+    ("negative_init", dict(I=-1), ">= 0"),
+    ("null_out", dict(out=None), "out"),
+    ("out_row_stride", dict(orow=8), "row stride"),
+    ("out_head_stride", dict(oh=10), "head stride"),
+    ("score_width", dict(sw=10, sr=10, sh=320), "width"),
+    ("null_seq", dict(seq=None), "seq_lens"),
+    ("heads", dict(heads=0), "heads"),
+]
+
+
+@pytest.mark.parametrize("label,kw,msg", BAD_TOPK, ids=[b[0] for b in BAD_TOPK])
+def test_topk_rules(label, kw, msg):
+    assert _topk(**kw) == B.MM3_EINVAL
+    assert msg in _err(), _err()
+
+
+def test_decode_workspace_rules():
+    p = _problem()
+    need = B.lib().mm3_index_decode_workspace_bytes(ctypes.byref(p), 16, 0)
+    assert need == 4 * 32 * 64 * 4  # heads * tokens * round_up(64, 16) * fp32
+    assert B.lib().mm3_index_decode_workspace_bytes(ctypes.byref(p), 16, 1) == 0
+    for ws, nbytes in [(None, need), (FAKE * 7, need - 1), (FAKE * 7 + 16, need)]:
+        rc = B.lib().mm3_index_decode(ctypes.byref(p), 16, 1, 2, FAKE * 6, 32 * 16, 16, None, 0, 0,
+                                      0, ws, nbytes, None)
+        assert rc == B.MM3_EWORKSPACE, (ws, nbytes)
+        assert "workspace" in _err()
+    bad = _problem(heads=0)
+    assert B.lib().mm3_index_decode_workspace_bytes(ctypes.byref(bad), 16, 0) == 0
+    assert "heads" in _err()
+
+
+def _sparse(**kw):
+    d = dict(ids=FAKE, orow=16, topk=16, seq=FAKE * 2, R=8, Q=4, msl=8192, abt=FAKE * 3, abt_row=128,
+             abt_w=128, P=2, stride=2, st=FAKE * 4, st_row=32, ctx=FAKE * 5)
+    d.update(kw)
+    return B.lib().mm3_build_sparse_block_table(d["ids"], d["orow"], d["topk"], d["seq"], d["R"],
+                                                d["Q"], d["msl"], d["abt"], d["abt_row"], d["abt_w"],
+                                                d["P"], d["stride"], d["st"], d["st_row"], d["ctx"],
+                                                None)
+
+
+BAD_SPARSE = [
+    ("missing_table", dict(abt=None), "together"),
+    ("missing_ctx", dict(ctx=None), "together"),
+    ("stride", dict(stride=3), "block_page_stride"),
+    ("narrow_abt", dict(abt_w=127, abt_row=127), "narrower"),
+    ("st_row", dict(st_row=31), "sparse table row stride"),
+    ("pages", dict(P=0, stride=0), "pages_per_block"),
+]
+
+
+@pytest.mark.parametrize("label,kw,msg", BAD_SPARSE, ids=[b[0] for b in BAD_SPARSE])
+def test_sparse_table_rules(label, kw, msg):
+    assert _sparse(**kw) == B.MM3_EINVAL
+    assert msg in _err(), _err()
+
+
+def test_binding_rejects_wrong_dtypes_before_the_library():
+    import torch
+    q = torch.zeros((4, 1, 128), dtype=torch.float32)
+    k = torch.zeros((2, 128, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 16), dtype=torch.int32)
+    sl = torch.zeros((1,), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mm3.make_problem(q, k, bt, sl, 4, 2048, 0.1)
+    with pytest.raises(ValueError):
+        mm3.make_problem(q.bfloat16(), k, bt.long(), sl, 4, 2048, 0.1)

@@ -1,0 +1,104 @@
+"""The GPU parity checkers, exercised on the CPU with oracle outputs and
+planted mistakes (so a broken checker cannot pass a broken kernel)."""
+import numpy as np
+import pytest
+
+from tests import _parity as P
+from workloads import config, host_arrays
+
+
+@pytest.fixture(scope="module")
+def case():
+    w = config(2, device="cpu", R=4, lens=(300, 3000), max_seq_len=4096)
+    a = host_arrays(w)
+    s, ids = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
+    return w, a, s, ids
+
+
+def _inv(w, a, ids):
+    P.check_invariants(ids, a["seq_lens"], w.query_len, w.topk, w.init_blocks, w.local_blocks)
+
+
+def test_accepts_oracle_output(case):
+    w, a, s, ids = case
+    _inv(w, a, ids)
+    assert P.check_ids(ids, ids, s, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
+                       w.local_blocks) == 0
+    assert P.check_scores(s.copy(), s) == 0.0
+
+
+def _row_with_choice(w, a, ids):
+    """A (head, row) that has more visible blocks than topk."""
+    for t in range(ids.shape[1]):
+        pos = int(a["seq_lens"][t // w.query_len]) - w.query_len + t % w.query_len
+        if pos // 128 + 1 > w.topk:
+            return 1 % ids.shape[0], t, pos // 128 + 1
+    raise AssertionError("no row with a choice")
+
+
+@pytest.mark.parametrize("mistake", ["hole", "unsorted", "dup", "out_of_range", "drop_init",
+                                     "drop_local", "swap_worse"])
+def test_planted_id_mistakes_are_caught(case, mistake):
+    w, a, s, ids = case
+    h, t, nv = _row_with_choice(w, a, ids)
+    bad = ids.copy()
+    row = bad[h, t]
+    if mistake == "hole":
+        row[3] = -1
+    elif mistake == "unsorted":
+        row[[2, 3]] = row[[3, 2]]
+    elif mistake == "dup":
+        row[3] = row[2]
+    elif mistake == "out_of_range":
+        row[-1] = nv
+    elif mistake == "drop_init":
+        row[0] = [b for b in range(nv) if b not in row][0]
+        row.sort()
+    elif mistake == "drop_local":
+        row[-1] = [b for b in range(nv) if b not in row][0]
+        row.sort()
+    elif mistake == "swap_worse":
+        chosen = [b for b in row if b not in (0, nv - 1, nv - 2)]
+        rest = [b for b in range(nv) if b not in row]
+        worst_rest = min(rest, key=lambda b: s[h, t, b])
+        row[list(row).index(chosen[0])] = worst_rest
+        row.sort()
+    with pytest.raises(AssertionError):
+        _inv(w, a, bad)
+        P.check_ids(bad, ids, s, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
+                    w.local_blocks)
+
+
+def test_near_tie_is_accepted(case):
+    w, a, s, ids = case
+    h, t, nv = _row_with_choice(w, a, ids)
+    s2 = s.copy()
+    row = ids[h, t]
+    forced = {0, nv - 1, nv - 2}
+    kth_b = min((b for b in row if b not in forced), key=lambda b: s2[h, t, b])
+    out_b = max((b for b in range(nv) if b not in row), key=lambda b: s2[h, t, b])
+    s2[h, t, out_b] = s2[h, t, kth_b] - 1e-5  # within tolerance below the k-th
+    g = ids.copy()
+    g[h, t, list(row).index(kth_b)] = out_b
+    g[h, t].sort()
+    assert P.check_ids(g, ids, s2, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
+                       w.local_blocks) == 1
+
+
+def test_planted_score_mistakes_are_caught(case):
+    w, a, s, ids = case
+    g = s.copy()
+    vis = np.argwhere(~np.isnan(s))
+    h, t, b = vis[len(vis) // 2]
+    g[h, t, b] *= 1.01
+    with pytest.raises(AssertionError):
+        P.check_scores(g, s)
+    g = s.copy()
+    g[h, t, b] = np.nan  # unwritten visible entry
+    with pytest.raises(AssertionError):
+        P.check_scores(g, s)
+    g = s.copy()
+    inv = np.argwhere(np.isnan(s))[0]
+    g[tuple(inv)] = 0.0  # write outside the visible set
+    with pytest.raises(AssertionError):
+        P.check_scores(g, s)
