@@ -106,131 +106,387 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t x, u32x2 tab) {
 
 // ------------------------------------------------------------------ scorer
 
+// A wave scores one block (page) as two halves of 64 tokens.  Half h of the
+// page is held as 4 token tiles x 4 k-steps of MFMA A operands (bf16), or as
+// 4 tiles of 16 nibble bytes plus their 2 scale bytes (NVFP4).
 template <int KFMT>
-__global__ __launch_bounds__(256) void decode_score_kernel(ScoreArgs a) {
-  __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
-  const int r = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int seq = a.seq_lens[r];
-  if (seq <= 0) return;
-  const int nb = (seq - 1) / kBlock + 1;  // blocks the request's last row sees
-  const int b_begin = blockIdx.x * a.blocks_per_wg;
-  if (b_begin >= nb) return;
-  const int b_end = min(nb, b_begin + a.blocks_per_wg);
+struct HalfBuf;
+template <>
+struct HalfBuf<0> {
+  u32x4 v[4][4];
+};
+template <>
+struct HalfBuf<1> {
+  u32x4 nib[4];
+  uint32_t sc[4];
+};
 
-  if (KFMT == 1) {
-    lut[threadIdx.x].x = kFp4Lut.w[threadIdx.x][0];
-    lut[threadIdx.x].y = kFp4Lut.w[threadIdx.x][1];
-    __syncthreads();
-  }
-
-  // Query rows: MFMA column n is row c = j*H + h of this request.
-  const int H = a.heads, Q = a.qlen, HQ = H * Q;
-  int pos_n = -1, t_n = 0, h_n = 0;
+struct QRows {
   bf16x8 qb[4];
-  if (n < HQ) {
-    const int j = n / H;
-    h_n = n - j * H;
-    t_n = r * Q + j;
-    pos_n = seq - Q + j;
-    const uint16_t* qp = a.q + (int64_t)t_n * a.q_tok + (int64_t)h_n * a.q_head;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      if (KFMT == 0) {
-        // k-group g, step kc covers d = 32*kc + 8*g .. +8 (natural order)
-        qb[kc] = as_bf16x8(ld16(qp + 32 * kc + 8 * g));
-      } else {
-        // NVFP4 tiles hand lane group g the 32 dims [32g, 32g+32); step kc
-        // covers 8 of them in the order {0,2,4,6,1,3,5,7}
-        u32x4 v = ld16(qp + 32 * g + 8 * kc);
-        u32x4 p;
-        p.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // e0, e2
-        p.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // e4, e6
-        p.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // e1, e3
-        p.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // e5, e7
-        qb[kc] = as_bf16x8(p);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qb[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-  }
-  const int min_pos = seq - Q;  // position of the request's first row
-  const int32_t* bt_row = a.bt + (int64_t)r * a.bt_stride;
+  int pos;   // position of this lane's row (MFMA column n), -1 if none
+  int t;     // its token row
+  int h;     // its head
+};
 
-  for (int b = b_begin + wave; b < b_end; b += 4) {
-    const int64_t page = bt_row[b];
-    f32x4 acc[8];
-    if (KFMT == 0) {
-      const uint8_t* kp = a.kdata + page * (kBlock * kDim * 2);
-      u32x4 kr[8][4];
+// Raw query loads for one request, before the NVFP4 element reordering.
+struct QRaw {
+  u32x4 v[4];
+};
+
+// Buffer descriptor over [base, base + bytes); bytes == 0 makes every load
+// through it return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+
+// Issue the query loads of request r: column n = row j*H + h of the request.
+// Lanes without a row (n >= H*Q) and calls with live == false get zeros.
+template <int KFMT>
+__device__ __forceinline__ QRaw issue_q(const ScoreArgs& a, int r, int n, int g, bool live) {
+  const int H = a.heads, Q = a.qlen;
+  const int j = n / H, h = n - (n / H) * H;
+  const uint16_t* base = a.q + (int64_t)r * Q * a.q_tok;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base, live ? 0x7FFFFFF0 : 0);
+  const int row = n < H * Q ? (int)(((int64_t)j * a.q_tok + (int64_t)h * a.q_head) * 2) : 0x7FFFFFF0;
+  QRaw q;
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+  for (int kc = 0; kc < 4; ++kc) {
+    // bf16: k-group g, step kc covers d = 32*kc + 8*g .. +8 (natural order);
+    // NVFP4: lane group g takes the 32 dims [32g, 32g+32), step kc 8 of them
+    const int d = KFMT == 0 ? 32 * kc + 8 * g : 32 * g + 8 * kc;
+    q.v[kc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, row + d * 2, 0, 0));
+  }
+  return q;
+}
+
+// Finish the query operands of request r (row bookkeeping; NVFP4 element
+// order {0,2,4,6,1,3,5,7} within each 8-element step to match the keys).
+template <int KFMT>
+__device__ __forceinline__ void set_q(QRows& q, const QRaw& raw, const ScoreArgs& a, int r, int seq, int n) {
+  const int H = a.heads, Q = a.qlen;
+  const int j = n / H;
+  q.h = n - j * H;
+  q.t = r * Q + j;
+  q.pos = n < H * Q ? seq - Q + j : -1;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          kr[tt][kc] = ld16(kp + ((16 * tt + n) * kDim + 32 * kc + 8 * g) * 2);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) acc[tt] = mfma16(as_bf16x8(kr[tt][kc]), qb[kc], acc[tt]);
-      }
+  for (int kc = 0; kc < 4; ++kc) {
+    const u32x4 v = raw.v[kc];
+    if constexpr (KFMT == 0) {
+      q.qb[kc] = as_bf16x8(v);
     } else {
-      const uint8_t* kn = a.kdata + page * (kBlock * kDim / 2);
-      const uint8_t* ks = a.kscales + page * (kBlock * kDim / 16);
-      u32x4 nib[8];
-      uint32_t sc[8];
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        nib[tt] = ld16(kn + (16 * tt + n) * (kDim / 2) + 16 * g);
-        sc[tt] = *reinterpret_cast<const uint16_t*>(ks + (16 * tt + n) * (kDim / 16) + 2 * g);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const u32x2 t0 = lut[sc[tt] & 0xFF];
-        const u32x2 t1 = lut[sc[tt] >> 8];
-        acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[tt] = mfma16(as_bf16x8(fp4x8_to_bf16(nib[tt].x, t0)), qb[0], acc[tt]);
-        acc[tt] = mfma16(as_bf16x8(fp4x8_to_bf16(nib[tt].y, t0)), qb[1], acc[tt]);
-        acc[tt] = mfma16(as_bf16x8(fp4x8_to_bf16(nib[tt].z, t1)), qb[2], acc[tt]);
-        acc[tt] = mfma16(as_bf16x8(fp4x8_to_bf16(nib[tt].w, t1)), qb[3], acc[tt]);
-      }
+      u32x4 p;
+      p.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // e0, e2
+      p.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // e4, e6
+      p.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // e1, e3
+      p.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // e5, e7
+      q.qb[kc] = as_bf16x8(p);
     }
-    // acc[tt][i] = dot of token 16*tt + 4*g + i with row n
+  }
+}
+
+// Issue the loads of half `half` of a page.  The page base is wave-uniform
+// and goes into a buffer descriptor (scalar registers) sized to exactly one
+// page, so no load can leave the page; each lane keeps one 32-bit offset.
+// live == false issues the same instructions with an empty descriptor: they
+// return zeros and move no data, which keeps the loop free of branches
+// around loads (and the wait counts exact).
+template <int KFMT>
+__device__ __forceinline__ void issue_half(HalfBuf<KFMT>& buf, const ScoreArgs& a, int64_t page,
+                                           int half, int n, int g, bool live) {
+  if constexpr (KFMT == 0) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(a.kdata + page * (kBlock * kDim * 2), live ? kBlock * kDim * 2 : 0);
+    const int voff = n * (kDim * 2) + 16 * g;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        buf.v[tt][kc] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * kc, (4 * half + tt) * 4096, 0));
+  } else {
+    const __amdgpu_buffer_rsrc_t rn = rsrc(a.kdata + page * (kBlock * kDim / 2), live ? kBlock * kDim / 2 : 0);
+    const __amdgpu_buffer_rsrc_t rsc = rsrc(a.kscales + page * (kBlock * kDim / 16), live ? kBlock * kDim / 16 : 0);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      buf.nib[tt] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, n * (kDim / 2) + 16 * g, (4 * half + tt) * 1024, 0));
+      buf.sc[tt] = __builtin_amdgcn_raw_buffer_load_b16(rsc, n * (kDim / 16) + 2 * g, (4 * half + tt) * 128, 0);
+    }
+  }
+}
+
+// Multiply half `half` of a page by the query rows and fold its tokens into
+// this lane's running maximum m (lane l: row l%16, tokens 4*(l/16) + 0..3 of
+// each 16-token tile).  lim: token s of the block is visible iff s <= lim.
+template <int KFMT>
+__device__ __forceinline__ void compute_half(const HalfBuf<KFMT>& buf, const QRows& q, const u32x2* lut,
+                                             int half, bool full, int lim, int g, float& m) {
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KFMT == 0) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(buf.v[tt][kc]), q.qb[kc], acc);
+    } else {
+      const u32x2 t0 = lut[buf.sc[tt] & 0xFF];
+      const u32x2 t1 = lut[(buf.sc[tt] >> 8) & 0xFF];
+      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].x, t0)), q.qb[0], acc);
+      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].y, t0)), q.qb[1], acc);
+      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].z, t1)), q.qb[2], acc);
+      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].w, t1)), q.qb[3], acc);
+    }
+    if (full) {
+      m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+    } else {
+      const int s0 = 64 * half + 16 * tt + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s0 + i <= lim) m = fmaxf(m, acc[i]);
+    }
+  }
+}
+
+// The block a wave works on: request r, logical block b, the request's
+// length and the page the block table maps b to (all wave-uniform).
+struct Cur {
+  int r;
+  int b;
+  int seq;
+  int64_t page;
+};
+
+__device__ __forceinline__ int64_t page_of(const ScoreArgs& a, int r, int b) {
+  const int32_t __attribute__((address_space(4)))* bt =
+      (const int32_t __attribute__((address_space(4)))*)a.bt;
+  return bt[(int64_t)r * a.bt_stride + b];
+}
+
+// Score every block the walker hands this wave.  Loads run one block ahead:
+// while half 0 of block i is multiplied, half 1 of block i is in flight;
+// while half 1 is multiplied, the next block's query rows (on a request
+// change) and its half 0 are.  Every load is issued unconditionally (empty
+// descriptors where there is nothing to fetch).
+template <int KFMT, typename Walk>
+__device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut, Walk& walk) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int HQ = a.heads * a.qlen;
+  Cur cur;
+  if (!walk.first(cur)) return;
+  QRows q;
+  {
+    const QRaw raw = issue_q<KFMT>(a, cur.r, n, g, true);
+    set_q<KFMT>(q, raw, a, cur.r, cur.seq, n);
+  }
+  HalfBuf<KFMT> A, B;
+  issue_half<KFMT>(A, a, cur.page, 0, n, g, true);
+  issue_half<KFMT>(B, a, cur.page, 1, n, g, true);
+  while (true) {
+    Cur nxt = cur;
+    const bool has_next = walk.next(nxt);
+    const bool new_req = has_next && nxt.r != cur.r;
+    __builtin_amdgcn_sched_barrier(0);
+    const bool full = kBlock * cur.b + (kBlock - 1) <= cur.seq - a.qlen;
+    const int lim = q.pos - kBlock * cur.b;
     float m = -INFINITY;
-    if (kBlock * b + (kBlock - 1) <= min_pos) {
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
-        m = fmaxf(m, fmaxf(fmaxf(acc[tt][0], acc[tt][1]), fmaxf(acc[tt][2], acc[tt][3])));
-    } else {
-      const int lim = pos_n - kBlock * b;  // token s visible iff s <= lim
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * tt + 4 * g + i <= lim) m = fmaxf(m, acc[tt][i]);
-    }
+    compute_half<KFMT>(A, q, lut, 0, full, lim, g, m);
+    __builtin_amdgcn_sched_barrier(0);
+    const QRaw qn = issue_q<KFMT>(a, nxt.r, n, g, new_req);
+    issue_half<KFMT>(A, a, nxt.page, 0, n, g, has_next);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_half<KFMT>(B, q, lut, 1, full, lim, g, m);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_half<KFMT>(B, a, nxt.page, 1, n, g, has_next);
+    __builtin_amdgcn_sched_barrier(0);
     m = wave_max_xor(m, 16);
     m = wave_max_xor(m, 32);
-    if (g == 0 && n < HQ && pos_n >= kBlock * b)
-      a.scores[(int64_t)h_n * a.s_head + (int64_t)t_n * a.s_row + b] = m * a.sm_scale;
+    if (g == 0 && n < HQ && q.pos >= kBlock * cur.b)
+      a.scores[(int64_t)q.h * a.s_head + (int64_t)q.t * a.s_row + cur.b] = m * a.sm_scale;
+    if (!has_next) break;
+    if (new_req) set_q<KFMT>(q, qn, a, nxt.r, nxt.seq, n);
+    cur = nxt;
   }
 }
 
-static dim3 decode_grid(const ScoreArgs& a) {
-  const int chunks = (a.nb_max + a.blocks_per_wg - 1) / a.blocks_per_wg;
-  return dim3(chunks, a.num_reqs, 1);
+__device__ __forceinline__ void fill_lut(u32x2* lut) {
+  lut[threadIdx.x].x = kFp4Lut.w[threadIdx.x][0];
+  lut[threadIdx.x].y = kFp4Lut.w[threadIdx.x][1];
 }
 
-hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_score_kernel<0>, decode_grid(a), dim3(256), 0, s, a);
+// ---- length-balanced persistent scorer
+//
+// A fixed grid (a few workgroups per CU) shares all (request, block) pairs of
+// the batch equally: each workgroup builds the prefix sum of the requests'
+// block counts in LDS, takes one contiguous slice of the flattened block
+// list, and its four waves take every fourth block of the slice.  Every wave
+// streams pages continuously; no workgroup idles on a short request.
+
+struct BalancedWalk {
+  const ScoreArgs* a;
+  const int32_t* pre;  // LDS: pre[r] = blocks of requests < r
+  const int32_t* sl;   // LDS: seq_lens
+  int64_t gb, hi;      // this wave's next flattened block, slice end
+
+  __device__ __forceinline__ void fill(Cur& c) {
+    c.b = __builtin_amdgcn_readfirstlane((int)(gb - pre[c.r]));
+    c.seq = __builtin_amdgcn_readfirstlane(sl[c.r]);
+    // finish the LDS reads before the scalar page load, so that later waits
+    // on LDS never also wait on that load
+    __builtin_amdgcn_sched_barrier(0);
+    c.page = page_of(*a, c.r, c.b);
+  }
+  __device__ __forceinline__ bool first(Cur& c) {
+    if (gb >= hi) return false;
+    int lo = 0, up = a->num_reqs;  // last r with pre[r] <= gb
+    while (up - lo > 1) {
+      const int mid = (lo + up) >> 1;
+      if (pre[mid] <= gb) lo = mid; else up = mid;
+    }
+    c.r = __builtin_amdgcn_readfirstlane(lo);
+    fill(c);
+    return true;
+  }
+  __device__ __forceinline__ bool next(Cur& c) {
+    gb += 4;
+    if (gb >= hi) return false;
+    int r = c.r;
+    while (pre[r + 1] <= gb) ++r;
+    c.r = __builtin_amdgcn_readfirstlane(r);
+    fill(c);
+    return true;
+  }
+};
+
+template <int KFMT>
+__global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
+  extern __shared__ int32_t smem[];
+  __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
+  __shared__ int32_t part[256];
+  const int R = a.num_reqs;
+  int32_t* pre = smem;        // [R + 1]
+  int32_t* sl = smem + R + 1;  // [R]
+  const int per = (R + 255) / 256;
+  const int r0 = min(R, (int)threadIdx.x * per), r1 = min(R, r0 + per);
+  int sum = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int s = a.seq_lens[r];
+    sl[r] = s;
+    sum += s > 0 ? (s - 1) / kBlock + 1 : 0;
+  }
+  part[threadIdx.x] = sum;
+  if constexpr (KFMT == 1) fill_lut(lut);
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the partial sums
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int base = threadIdx.x ? part[threadIdx.x - 1] : 0;
+  for (int r = r0; r < r1; ++r) {
+    pre[r] = base;
+    const int s = sl[r];
+    base += s > 0 ? (s - 1) / kBlock + 1 : 0;
+  }
+  if (threadIdx.x == 255) pre[R] = part[255];
+  __syncthreads();
+  const int64_t total = pre[R];
+  const int64_t lo = total * blockIdx.x / gridDim.x;
+  const int64_t hi = total * (blockIdx.x + 1) / gridDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  BalancedWalk walk{&a, pre, sl, lo + wave, hi};
+  score_wave<KFMT>(a, lut, walk);
+}
+
+// ---- per-request chunk scorer (any batch size)
+//
+// Grid (block chunks, requests): workgroup (x, r) covers blocks
+// [x*bpw, (x+1)*bpw) of request r and returns at once past its end.
+
+struct ChunkWalk {
+  const ScoreArgs* a;
+  int r, seq, b, b_end;
+  __device__ __forceinline__ bool first(Cur& c) {
+    if (b >= b_end) return false;
+    c.r = r;
+    c.seq = seq;
+    c.b = b;
+    c.page = page_of(*a, r, b);
+    return true;
+  }
+  __device__ __forceinline__ bool next(Cur& c) {
+    b += 4;
+    if (b >= b_end) return false;
+    c.b = b;
+    c.page = page_of(*a, r, b);
+    return true;
+  }
+};
+
+template <int KFMT>
+__global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
+  __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
+  const int r = blockIdx.y;
+  const int seq = a.seq_lens[r];
+  if (seq <= 0) return;
+  const int nb = (seq - 1) / kBlock + 1;
+  const int b_begin = blockIdx.x * a.blocks_per_wg;
+  if (b_begin >= nb) return;
+  if constexpr (KFMT == 1) {
+    fill_lut(lut);
+    __syncthreads();
+  }
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  ChunkWalk walk{&a, r, seq, b_begin + wave, min(nb, b_begin + a.blocks_per_wg)};
+  score_wave<KFMT>(a, lut, walk);
+}
+
+// ------------------------------------------------------------------ launch
+
+// Largest batch whose lengths and prefix sums fit the balanced scorer's LDS.
+constexpr int kBalancedMaxReqs = 8192;
+
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Workgroups of the balanced scorer resident per CU with `lds` bytes of
+// dynamic LDS (cached per 1 KiB step of LDS).
+template <int KFMT>
+static int balanced_occupancy(size_t lds) {
+  static int cache[(2 * kBalancedMaxReqs + 1) * 4 / 1024 + 2] = {0};
+  const size_t key = (lds + 1023) / 1024;
+  if (!cache[key]) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_score_balanced<KFMT>, 256, key * 1024) !=
+            hipSuccess || v <= 0)
+      v = 1;
+    cache[key] = v;
+  }
+  return cache[key];
+}
+
+template <int KFMT>
+static hipError_t launch_decode(const ScoreArgs& a, hipStream_t s) {
+  if (a.num_reqs <= kBalancedMaxReqs) {
+    const size_t lds = (size_t)(2 * a.num_reqs + 1) * sizeof(int32_t);
+    const int grid = device_cus() * balanced_occupancy<KFMT>(lds);
+    hipLaunchKernelGGL(decode_score_balanced<KFMT>, dim3(grid), dim3(256), lds, s, a);
+  } else {
+    const int chunks = (a.nb_max + a.blocks_per_wg - 1) / a.blocks_per_wg;
+    hipLaunchKernelGGL(decode_score_chunked<KFMT>, dim3(chunks, a.num_reqs, 1), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_score_kernel<1>, decode_grid(a), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
+hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s) { return launch_decode<0>(a, s); }
+
+hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s) { return launch_decode<1>(a, s); }
 
 }  // namespace mm3
