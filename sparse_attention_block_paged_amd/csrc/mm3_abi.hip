@@ -129,6 +129,9 @@ ScoreArgs score_args(const mm3_problem* p, float* s, int64_t sh, int64_t sr) {
   int bpw = 4;  // blocks per workgroup (4 waves)
   while (bpw < 32 && total / bpw > 8192) bpw *= 2;
   a.blocks_per_wg = bpw;
+  const int64_t T = (int64_t)p->num_reqs * p->query_len;
+  const int64_t extent = T == 0 ? 0 : ((int64_t)(p->heads - 1) * sh + (T - 1) * sr + a.nb_max) * 4;
+  a.s_bytes = extent <= 0x7FFFFFC0 ? (int32_t)extent : 0;
   return a;
 }
 

@@ -26,6 +26,8 @@ struct ScoreArgs {
   int32_t nb_max;           // cdiv(max_seq_len, 128)
   int32_t blocks_per_wg;    // decode: blocks one workgroup covers
   int32_t nsplit;           // prefill: block splits per row tile
+  int32_t s_bytes;          // bytes from scores to one past its last element
+                            // (0 when that exceeds 2^31 - 64)
   float sm_scale;
 };
 
