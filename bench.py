@@ -43,7 +43,42 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU work for the oracle baseline")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run a 1 GiB device copy first (reference for HBM counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="summarise rocprofv3 CSV output in DIR and exit (no GPU)")
+    ap.add_argument("--label", default="", help="label for --summarize-rocprof")
+    ap.add_argument("--record-traffic", action="store_true",
+                    help="with --summarize-rocprof: record counter traffic in profiles/traffic.json")
     return ap.parse_args()
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+CALIB_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: recorded HBM traffic is only reported while
+    the kernels are the ones the counters were taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_block_paged_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    ent = rec.get(workload, {})
+    if ent.get("source_hash") != kernel_source_hash() or ent.get("kernel") != kernel:
+        return None
+    return ent.get("bytes_per_launch")
 
 
 def algorithmic(w, seq):
@@ -71,6 +106,9 @@ def algorithmic(w, seq):
 
 def main():
     args = parse()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.label, args.record_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs the indexer on one GPU; --gpus above 1 is not "
@@ -147,6 +185,14 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms
 
+    if args.calibrate:  # known-size copy: scale reference for FETCH_SIZE / WRITE_SIZE
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # whole step (the contract's timed region)
     for i in range(args.warmup):
         step(i)
@@ -173,13 +219,15 @@ def main():
         achieved = alg["flops"] / (ms_score * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                    traffic=None, kernel="prefill_score_kernel", ms=round(ms_score, 4),
+                    traffic=recorded_traffic(base.name, "prefill_score_kernel"),
+                    kernel="prefill_score_kernel", ms=round(ms_score, 4),
                     per_launch_flops=alg["flops"])
     else:
         achieved = alg["scorer_bytes"] / (ms_score * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="decode_score_kernel<%d>" % base.kfmt, ms=round(ms_score, 4),
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=recorded_traffic(base.name, "decode_score_balanced<%d>" % base.kfmt),
+                    kernel="decode_score_balanced<%d>" % base.kfmt, ms=round(ms_score, 4),
                     per_launch_bytes=alg["scorer_bytes"])
     sel_gbs = alg["selector_bytes"] / (ms_topk * 1e-3) / 1e9
 
@@ -225,6 +273,69 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_rocprof(d, label, record):
+    """Print a short summary of rocprofv3 CSV output found under d: kernel
+    statistics (--kernel-trace --stats), or per-dispatch counters (--pmc),
+    with FETCH_SIZE / WRITE_SIZE scaled by what the same counter reads for
+    the 1 GiB calibration copy."""
+    import glob
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    pmc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        rows = _read_csv(stats[0])
+        print(f"# kernel statistics ({label})")
+        print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total%':>7s}")
+        for r in rows[:12]:
+            name = r.get("Name", r.get("KernelName", "?"))
+            print(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
+                  f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} {float(r['Percentage']):7.2f}")
+    if pmc:
+        rows = _read_csv(pmc[0])
+        per = {}
+        for r in rows:
+            key = (r.get("Kernel_Name", r.get("Kernel-Name", "?")), r.get("Counter_Name"))
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
+        counters = sorted({k[1] for k in per})
+        print(f"# per-dispatch counters ({label}); mean over dispatches")
+        # the three calibration copies are the largest copy dispatches when the
+        # run uses --copies 1 (no pool clone); take their median
+        calib = {}
+        for (kern, cname), vals in sorted(per.items()):
+            if "copyBuffer" in kern and cname in ("FETCH_SIZE", "WRITE_SIZE"):
+                top = sorted(vals)[-3:]
+                calib[cname] = top[len(top) // 2]
+        for (kern, cname), vals in sorted(per.items()):
+            mean = sum(vals) / len(vals)
+            extra = ""
+            if cname in calib and calib[cname] > 0:
+                scale = (CALIB_BYTES / 1024.0) / calib[cname]
+                extra = f"  scaled bytes {mean * 1024 * scale:.4g} (copy scale {scale:.4f})"
+            print(f"{kern[:60]:60s} {cname:14s} n={len(vals):4d} mean={mean:14.1f}{extra}")
+        if record:
+            path = os.path.join(PROFILES, "traffic.json")
+            rec = json.load(open(path)) if os.path.exists(path) else {}
+            for (kern, cname), vals in per.items():
+                short = kern.split("(")[0].replace("void ", "").replace("mm3::", "")
+                if not short.startswith(("decode_score_balanced", "prefill_score_kernel")):
+                    continue
+                if cname not in calib:
+                    continue
+                scale = (CALIB_BYTES / 1024.0) / calib[cname]
+                ent = rec.setdefault(label, {})
+                ent["kernel"] = short
+                ent["source_hash"] = kernel_source_hash()
+                ent.setdefault("counters", {})[cname] = sum(vals) / len(vals) * 1024 * scale
+                ent["bytes_per_launch"] = round(sum(ent["counters"].values()))
+            json.dump(rec, open(path, "w"), indent=1, sort_keys=True)
+            print(f"recorded -> {path}")
 
 
 def cpu_baseline(w, seq, seconds):
