@@ -80,8 +80,13 @@ extern "C" {
  *                aligned, num_pages >= 1; kscales NULL for bf16.
  *   block_table  int32, entry (r, b) at block_table[r*bt_row_stride + b];
  *                bt_width >= cdiv(max_seq_len, 128); bt_row_stride >= bt_width.
- *   seq_lens     int32 [num_reqs], contiguous.
- *   query_len    rows per request, >= 1.
+ *   seq_lens     int32 [num_reqs], contiguous; each in [0, max_seq_len], and
+ *                block_table entries (r, b < cdiv(seq_lens[r], 128)) in
+ *                [0, num_pages).  Both live on the device and are not checked:
+ *                values outside these ranges make the kernels read out of
+ *                bounds.
+ *   query_len    rows per request, >= 1; num_reqs * query_len and
+ *                heads * query_len below 2^31.
  *   max_seq_len  capture-stable bound on every seq_lens[r] (e.g. the model's
  *                maximum length, not the batch maximum); sizes the grids.
  *   sm_scale     finite, > 0.

@@ -757,7 +757,7 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
 // Largest batch whose lengths and prefix sums fit the cooperative scorer's LDS.
 constexpr int kBalancedMaxReqs = 8192;
 
-static int device_cus() {
+int device_cus() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -50,6 +50,8 @@ int check_problem(const mm3_problem* p) {
   if (p->query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1, got %d", p->query_len);
   if (p->num_reqs < 0) return fail(MM3_EINVAL, "num_reqs must be >= 0, got %d", p->num_reqs);
   if (p->max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
+  if ((int64_t)p->num_reqs * p->query_len > INT32_MAX || (int64_t)p->heads * p->query_len > INT32_MAX)
+    return fail(MM3_EINVAL, "num_reqs * query_len and heads * query_len must be below 2^31");
   const int64_t nb = cdiv64(p->max_seq_len, MM3_BLOCK);
   if (nb > MM3_MAX_BLOCKS)
     return fail(MM3_EINVAL, "cdiv(max_seq_len,128) = %lld must be below 65535", (long long)nb);

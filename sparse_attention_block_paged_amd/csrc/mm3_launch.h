@@ -25,7 +25,6 @@ struct ScoreArgs {
   int32_t num_reqs;
   int32_t nb_max;           // cdiv(max_seq_len, 128)
   int32_t blocks_per_wg;    // decode: blocks one workgroup covers
-  int32_t nsplit;           // prefill: block splits per row tile
   int32_t s_bytes;          // bytes from scores to one past its last element
                             // (0 when that exceeds 2^31 - 64)
   float sm_scale;
@@ -73,7 +72,10 @@ hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s);
 
 // Rows one decode-scorer MFMA tile holds (heads * query_len must fit).
 constexpr int kDecodeRows = 16;
-// Flattened (token, head) rows of one prefill workgroup tile.
-constexpr int kPrefillRows = 256;
+// Flattened (token, head) rows of one prefill row tile.
+constexpr int kPrefillRows = 512;
+
+// Compute units of the current device (cached per device).
+int device_cus();
 
 }  // namespace mm3

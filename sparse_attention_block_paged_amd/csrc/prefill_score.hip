@@ -1,173 +1,387 @@
 // prefill_score.hip -- MFMA block scorer for chunked prefill on gfx950.
 //
 // What it computes (page "vllm.models.minimax_m3.amd.ops.index_topk",
-// minimax_m3_index_score: per query token and head, "the max over a 128-token
-// index-K block" for each visible block; causal within the chunk).
+// minimax_m3_index_score: per query token and head, the largest scaled
+// dot product over the causally visible keys of each 128-token index-K
+// block; causal within the chunk).
 //
 // Design.  With many query rows per request the score is a dense product
 // [rows x 128] . [128 x keys] followed by a max over each 128-key block, so it
-// runs on the bf16 matrix cores:
-//   * a workgroup owns 256 flattened (position, head) rows of one request --
-//     all heads of a position share its causal bound -- and a range of key
-//     blocks; wave w owns rows 64w..64w+63 as two 32-row MFMA B tiles held in
-//     registers (the queries are read once per workgroup);
-//   * each key page (32 KiB) is copied once per workgroup into LDS by direct
-//     global->LDS DMA (no registers), double buffered, with a 16-byte-chunk
-//     XOR swizzle (chunk c of token s at c ^ (s & 15)) so the A-operand reads
-//     of 32 tokens x 16 B are free of bank conflicts;
+// runs on the bf16 matrix cores.
+//   * Work unit: 512 flattened (position, head) rows of one request -- all
+//     heads of a position share its causal bound -- against one key block.
+//     A request's row tile x has one step per block it can see.  The steps of
+//     all tiles of all requests form one list; each persistent workgroup takes
+//     an equal contiguous share of it (a prefix scan over the tiles finds the
+//     start), so the chip stays full to the end whatever the causal triangle
+//     and the length mix look like.  Every (row, block) score is produced by
+//     exactly one step: shares need no merge.
+//   * Wave w owns rows 128w..128w+127 of the tile as four 32-row MFMA B tiles
+//     held in registers (loaded again only when the share crosses into the
+//     next tile); each key fragment read from LDS feeds four MFMAs.
+//   * Key pages (32 KiB) go global -> LDS by direct DMA (no registers), double
+//     buffered one block ahead, with a 16-byte-chunk XOR swizzle (chunk c of
+//     token s at c ^ (s & 15)) so the A-operand reads of 32 tokens x 16 B are
+//     free of bank conflicts.
 //   * v_mfma_f32_32x32x16_bf16 with keys as A (rows = tokens) and queries as
-//     B (columns = rows): each lane holds one query row and 16 tokens per
-//     tile, so the block max is an in-register max over 4 tiles x 16 values
-//     plus one cross-lane step (l ^ 32), fused into the epilogue; the causal
-//     mask is applied only on blocks that cross a row's position.
-// Work splits by (row tile, request, block range); every (row, block) score
-// is complete inside one workgroup, so splits need no merge.  Scores are
-// staged in LDS and written at the end as row-contiguous runs of 16 blocks:
-// storing each (row, block) value as it is produced scatters 4-byte writes
-// over 64 rows per instruction, which costs several times the score volume
-// in partial-line write-backs.
+//     B (columns = rows): each lane holds one query row and 16 tokens per tile,
+//     so the block max is an in-register max plus one cross-lane step (l ^ 32);
+//     the causal mask is applied only on blocks that cross a row's position.
+//   * Each wave stages its rows' scores in LDS and writes them every 8 blocks
+//     as row-contiguous 32-byte runs (one 4-byte store per row and block would
+//     scatter over 64 rows per instruction).
+// Two workgroups (80 KiB of LDS each) share a CU, so one's barrier or copy
+// wait is covered by the other's multiplies.
 #include "mm3_device.h"
 #include "mm3_launch.h"
 
 namespace mm3 {
 
-constexpr int kPageBytes = kBlock * kDim * 2;  // 32 KiB
-constexpr int kPrefillBlocksPerSplit = 16;
+constexpr int kPageBytes = kBlock * kDim * 2;              // 32 KiB
+constexpr int kPfWaves = 4;                                  // waves per workgroup
+constexpr int kPfWaveRows = 128;                             // query rows per wave
+static_assert(kPfWaves * kPfWaveRows == kPrefillRows, "row tile");
+constexpr int kPfStage = 8;                                  // blocks staged per write-out
+#ifndef MM3_PF_AHEAD
+#define MM3_PF_AHEAD 3
+#endif
+constexpr int kPfAhead = MM3_PF_AHEAD;                       // k-steps a fragment read runs ahead
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfCopies = kPageBytes / (kPfThreads * 16);    // 16-byte copies per thread per page
+constexpr int kPfStageFloats = kPfWaveRows * kPfStage;       // per wave
+constexpr int kPfLds = 2 * kPageBytes + kPfWaves * kPfStageFloats * 4;  // 80 KiB
+// Above this many (request, row tile) units the start-finding scan of the
+// balanced grid costs more than it saves: one workgroup per unit instead.
+constexpr int kPfBalancedMaxUnits = 1 << 16;
 
+#define MM3_AS3 __attribute__((address_space(3)))
+#define MM3_AS4 __attribute__((address_space(4)))
 
 __device__ __forceinline__ int swz(int tok, int chunk) {
   return tok * (kDim * 2) + ((chunk ^ (tok & 15)) << 4);
 }
 
-// Copy key page `page` into LDS buffer kl with the chunk swizzle of swz():
-// DMA instruction u of wave w fills LDS bytes [(4u + w) KiB, +1 KiB), lane l
-// the 16-byte slot of token t = 4(4u + w) + l/16 at position l%16, which
-// holds chunk (l%16) ^ (t & 15) of that token.  No registers are involved.
-__device__ __forceinline__ void dma_page(uint8_t* kl, const uint8_t* kdata, int64_t page, int wave, int lane) {
-  const uint8_t* kp = kdata + page * kPageBytes;
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Blocks that the last row of row tile x can see (0 if none): the tile's
+// step count.  Rows are ordered by position, so the last row bounds them all.
+__device__ __forceinline__ int tile_blocks(int seq, int x, int H, int Q, int HQ) {
+  const int rl = min(HQ, (x + 1) * kPrefillRows) - 1;
+  const int pl = seq - Q + rl / H;
+  return pl < 0 ? 0 : pl / kBlock + 1;
+}
+
+// One 16-byte global -> LDS copy per lane: LDS bytes [lds, lds + 1 KiB) get
+// the 64 lanes' 16-byte pieces at gbase + voff, in lane order.  Written as
+// assembly so the compiler does not track it (it cannot tell the two page
+// buffers apart and would wait for every copy in flight before each LDS
+// read); the ring's explicit waits and barriers order it.  The compiler
+// treats M0 as reserved (a clobber of it is ignored); no compiler-generated
+// code in this kernel reads M0, so the asm may set it freely.
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds, const uint8_t* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(gbase)
+               : "memory");
+}
+
+// Wait for this thread's copies (and any other vector memory access), then a
+// workgroup barrier.  The empty asm keeps LDS accesses from moving across it.
+__device__ __forceinline__ void ring_sync() {
+  asm volatile("" ::: "memory");
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Position in the list of (unit, block) steps.
+struct PfCursor {
+  int u, r, x, seq, nv, b;
+};
+
+template <bool BALANCED>
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs a, int units, int tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
+  uint8_t* const kbuf0 = smem;
+  uint8_t* const kbuf1 = smem + kPageBytes;
+  float* const stage_all = reinterpret_cast<float*>(smem + 2 * kPageBytes);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.heads, Q = a.qlen, HQ = H * Q;
+  const int32_t MM3_AS4* seq_s = (const int32_t MM3_AS4*)a.seq_lens;
+  const int32_t MM3_AS4* bt_s = (const int32_t MM3_AS4*)a.bt;
+
+  auto unit_at = [&](PfCursor& c, int u) {
+    c.u = u;
+    c.r = u / tiles;
+    c.x = u - c.r * tiles;
+    c.seq = seq_s[c.r];
+    c.nv = tile_blocks(c.seq, c.x, H, Q, HQ);
+  };
+  // next step of the list (callers guarantee one exists)
+  auto advance = [&](PfCursor& c) {
+    if (++c.b < c.nv) return;
+    do {
+      unit_at(c, c.u + 1);
+    } while (c.nv == 0);
+    c.b = 0;
+  };
+
+  // ---- this workgroup's share: steps [s0, s0 + nsteps) of the list
+  PfCursor cur;
+  int nsteps;
+  if constexpr (BALANCED) {
+    int* const scan = reinterpret_cast<int*>(stage_all);  // scratch until the first block
+    const int t = threadIdx.x;
+    const int lo = (int)((int64_t)units * t / kPfThreads);
+    const int hi = (int)((int64_t)units * (t + 1) / kPfThreads);
+    int part = 0;
+    for (int v = lo; v < hi; ++v) {
+      const int r = v / tiles;
+      part += tile_blocks(a.seq_lens[r], v - r * tiles, H, Q, HQ);
+    }
+    int incl = part;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int t = 4 * (4 * u + wave) + (lane >> 4);
-    const int c = (lane & 15) ^ (t & 15);
-    __builtin_amdgcn_global_load_lds((const void*)(kp + t * (kDim * 2) + c * 16),
-                                     (__attribute__((address_space(3))) void*)(kl + (4 * u + wave) * 1024), 16,
-                                     0, 0);
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) scan[wave] = incl;
+    __syncthreads();
+    int pre = incl - part, total = 0;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) {
+      const int sw = scan[w];
+      pre += w < wave ? sw : 0;
+      total += sw;
+    }
+    total = __builtin_amdgcn_readfirstlane(total);
+    // Workgroups are dealt to the 8 XCDs round-robin; renumber so that each
+    // XCD takes one contiguous stretch of the list (its requests' pages stay
+    // in its own L2).
+    const int G = gridDim.x, g = blockIdx.x;
+    const int lg = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
+    const int64_t s0 = (int64_t)total * lg / G;
+    nsteps = (int)((int64_t)total * (lg + 1) / G - s0);
+    if (part > 0 && pre <= s0 && s0 < pre + part) {
+      int acc = pre;
+      for (int v = lo; v < hi; ++v) {
+        const int r = v / tiles;
+        const int n = tile_blocks(a.seq_lens[r], v - r * tiles, H, Q, HQ);
+        if (s0 < acc + n) {
+          scan[8] = v;
+          scan[9] = (int)(s0 - acc);
+          break;
+        }
+        acc += n;
+      }
+    }
+    __syncthreads();
+    if (nsteps == 0) return;  // workgroup-uniform
+    unit_at(cur, __builtin_amdgcn_readfirstlane(scan[8]));
+    cur.b = __builtin_amdgcn_readfirstlane(scan[9]);
+  } else {
+    unit_at(cur, blockIdx.x);
+    cur.b = 0;
+    nsteps = cur.nv;
+    if (nsteps == 0) return;
+  }
+
+  // ---- this wave's query rows of the current tile
+  const int nl = lane & 31, kg = lane >> 5;
+  bf16x8 qb[4][8];
+  int pos_q[4];
+  int wave_pos_min = 0, wave_pos_max = -1;
+  bool wave_live = false;
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const int wrow0 = cur.x * kPrefillRows + kPfWaveRows * wave;
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const int i = wrow0 + 32 * qt + nl;
+      const bool ok = i < HQ;
+      const int ic = ok ? i : HQ - 1;
+      const int j = ic / H, h = ic - j * H;
+      pos_q[qt] = ok ? cur.seq - Q + j : -1;
+      const uint16_t* qp = a.q + (int64_t)(cur.r * Q + j) * a.q_tok + (int64_t)h * a.q_head;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) qb[qt][kk] = as_bf16x8(ld16(qp + 16 * kk + 8 * kg));
+    }
+    wave_live = wrow0 < HQ;
+    wave_pos_min = cur.seq - Q + min(wrow0, HQ - 1) / H;
+    wave_pos_max = cur.seq - Q + min(wrow0 + kPfWaveRows - 1, HQ - 1) / H;
+    // land them now: a query load still pending at the loop would make the
+    // compiler wait inside every step, and so on the copies in flight
+    wait_vmcnt<0>();
+  };
+
+  // ---- page copies.  Copy k of wave w fills LDS bytes [(4k + w) KiB, +1 KiB):
+  // lane l the 16-byte slot of token t = 16k + t0 (t0 = 4w + l/16) at slot
+  // l%16, which holds chunk (l%16) ^ (t & 15) of the token (t & 15 == t0).
+  const int t0 = 4 * wave + (lane >> 4);
+  const uint32_t src0 = t0 * (kDim * 2) + (((lane & 15) ^ t0) << 4);
+  auto copy_page = [&](uint8_t* kl, const PfCursor& c) __attribute__((always_inline)) {
+    const uint8_t* pg = a.kdata + (int64_t)bt_s[(int64_t)c.r * a.bt_stride + c.b] * kPageBytes;
+    const uint32_t l0 = (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)kl + 1024 * wave;
+    // the 4 KiB steps go on the scalar base: one offset register for all
+#pragma unroll
+    for (int k = 0; k < kPfCopies; ++k) copy16_to_lds(l0 + 4096 * k, pg + 4096 * k, src0);
+  };
+
+  float* const stage = stage_all + wave * kPfStageFloats;
+  // stage layout: row rho (0..127 of the wave), column c at rho*8 + (c ^ (rho & 7))
+  auto compute = [&](const uint8_t* kl, int b, int col) __attribute__((always_inline)) {
+    if (!(wave_live && wave_pos_max >= kBlock * b)) return;
+    // every row of the wave sees the whole block
+    const bool full = kBlock * b + (kBlock - 1) <= wave_pos_min;
+    float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // Key fragment of step st: tokens 32(st/8) + nl, 16-byte chunk
+    // 2(st%8) + kg, at swz().  With tok & 15 == nl & 15 == 2p + e, the chunk
+    // slot (2kk + kg) ^ (2p + e) is 2(kk ^ p) + (kg ^ e), so the address is
+    // a0 ^ (kk << 5) plus 8 KiB per token tile, a0 holding the kk = 0 slot
+    // (the buffers are 256-byte aligned, so bits 5..7 of a0 are exactly p).
+    // The asm hides a0's loop invariance: hoisted out of the step loop, the
+    // eight per-kk addresses would stay live next to the 192 query and
+    // accumulator registers and spill.
+    uint32_t a0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)kl + nl * (kDim * 2) +
+                  (((kg ^ nl) & 1) << 4) + (((nl >> 1) & 7) << 5);
+    asm volatile("" : "+v"(a0));
+    auto frag = [&](int st) {
+      const uint32_t addr = (a0 ^ ((st & 7) << 5)) + (st >> 3) * 32 * (kDim * 2);
+      return as_bf16x8(*(const MM3_AS3 u32x4*)(uintptr_t)addr);
+    };
+    // Fragments are read kPfAhead steps before their multiplies; the
+    // scheduling barrier at the end of each step pins that order (left
+    // alone, the scheduler sinks each read next to its use and the wave then
+    // waits out the full LDS latency at every step).
+    // Fragments are read kPfAhead steps before their multiplies; the
+    // scheduling barrier at the end of each step pins that order (left
+    // alone, the scheduler sinks each read next to its use and the wave then
+    // waits out the full LDS latency at every step).
+    bf16x8 fr[kPfAhead + 1];
+#pragma unroll
+    for (int p = 0; p < kPfAhead; ++p) fr[p] = frag(p);
+    f32x16 acc[4];
+#pragma unroll
+    for (int st = 0; st < 32; ++st) {
+      const int tt = st >> 3, kk = st & 7;
+      if (st + kPfAhead < 32) fr[(st + kPfAhead) % (kPfAhead + 1)] = frag(st + kPfAhead);
+      if (kk == 0) acc[0] = acc[1] = acc[2] = acc[3] = f32x16{};
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) acc[qt] = mfma32(fr[st % (kPfAhead + 1)], qb[qt][kk], acc[qt]);
+      if (kk == 7) {
+        // acc[qt][i]: token 32tt + 8(i/4) + 4kg + i%4 against row nl of tile qt
+        if (full) {
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m[qt] = fmaxf(m[qt], acc[qt][i]);
+        } else {
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) {
+            // visible iff 8(i/4) + i%4 <= pos - 128b - 32tt - 4kg
+            const int d = pos_q[qt] - kBlock * b - 32 * tt - 4 * kg;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              m[qt] = fmaxf(m[qt], 8 * (i >> 2) + (i & 3) <= d ? acc[qt][i] : -INFINITY);
+          }
+        }
+      }
+      // also keeps the next tile's multiplies (fresh accumulators) below the
+      // max: overlapping them needs a second set of 64 accumulator
+      // registers, which the two-waves-per-SIMD budget does not have (the
+      // other wave on the SIMD fills the matrix pipe meanwhile)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) m[qt] = wave_max_xor(m[qt], 32);
+    // lane (nl, kg) stages rows 64kg + nl and 64kg + 32 + nl (tiles 2kg, 2kg+1)
+    const int r0 = 64 * kg + nl, r1 = r0 + 32;
+    stage[r0 * kPfStage + (col ^ (r0 & 7))] = (kg ? m[2] : m[0]) * a.sm_scale;
+    stage[r1 * kPfStage + (col ^ (r1 & 7))] = (kg ? m[3] : m[1]) * a.sm_scale;
+  };
+
+  // write staged columns [0, nst) = blocks bfirst.. of the wave's rows; only
+  // visible (row, block) entries are written
+  auto flush = [&](int bfirst, int nst) __attribute__((always_inline)) {
+    const int c = lane & 7;
+    const int b = bfirst + c;
+    // not unrolled: unrolled, the compiler keeps every row's address live
+    // through the whole loop and spills
+#pragma unroll 1
+    for (int k = 0; k < kPfWaveRows / 8; ++k) {
+      const int rho = 8 * k + (lane >> 3);
+      const int i = cur.x * kPrefillRows + kPfWaveRows * wave + rho;
+      if (c < nst && i < HQ) {
+        const int j = i / H, h = i - j * H;
+        if (cur.seq - Q + j >= kBlock * b)
+          a.scores[(int64_t)h * a.s_head + (int64_t)(cur.r * Q + j) * a.s_row + b] =
+              stage[rho * kPfStage + (c ^ (rho & 7))];
+      }
+    }
+  };
+
+  // ---- the ring: block of step i sits in buffer i & 1; the copy of step
+  // i + 1 is started once every wave is past step i - 1.
+  load_q();
+  PfCursor nxt = cur;
+  copy_page(kbuf0, nxt);
+  int bfirst = cur.b, nst = 0;
+  for (int i = 0; i < nsteps; ++i) {
+    uint8_t* const kl = (i & 1) ? kbuf1 : kbuf0;
+    ring_sync();
+    if (i + 1 < nsteps) {
+      advance(nxt);
+      copy_page((i & 1) ? kbuf0 : kbuf1, nxt);
+    }
+    compute(kl, cur.b, nst);
+    ++nst;
+    const bool last = i + 1 == nsteps;
+    const bool tile_end = cur.b + 1 == cur.nv;
+    if (nst == kPfStage || tile_end || last) {
+      flush(bfirst, nst);
+      nst = 0;
+      bfirst = cur.b + 1;
+    }
+    if (!last) {
+      advance(cur);
+      if (cur.b == 0) {
+        bfirst = 0;
+        load_q();
+      }
+    }
   }
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_score_kernel(ScoreArgs a) {
-  // two page buffers as separate arrays, so reads of one never wait on the
-  // copy into the other
-  __shared__ __attribute__((aligned(16))) uint8_t kl0[kPageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t kl1[kPageBytes];
-  // block scores of the tile's rows, written out row-contiguous at the end;
-  // column j of row i sits at j ^ (i & 15) (spreads one column over banks)
-  __shared__ float sstage[kPrefillRows * kPrefillBlocksPerSplit];
-  const int r = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seq = a.seq_lens[r];
-  const int H = a.heads, Q = a.qlen, HQ = H * Q;
-  const int row0 = blockIdx.x * kPrefillRows;  // first flattened row of the tile
-  const int row_last = min(HQ, row0 + kPrefillRows) - 1;
-  const int pos_last = seq - Q + row_last / H;
-  if (pos_last < 0) return;
-  const int nv_tile = pos_last / kBlock + 1;
-  const int b_begin = blockIdx.z * kPrefillBlocksPerSplit;
-  if (b_begin >= nv_tile) return;
-  const int b_end = min(nv_tile, b_begin + kPrefillBlocksPerSplit);
-
-  // This lane's two query rows (one per 32-row tile) and their B operands.
-  const int nl = lane & 31, kg = lane >> 5;
-  int pos_q[2];
-  bf16x8 qb[2][8];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int i = row0 + 64 * wave + 32 * qt + nl;
-    const bool ok = i < HQ;
-    const int ic = ok ? i : HQ - 1;
-    const int j = ic / H, h = ic - (ic / H) * H;
-    pos_q[qt] = ok ? seq - Q + j : -1;
-    const uint16_t* qp = a.q + (int64_t)(r * Q + j) * a.q_tok + (int64_t)h * a.q_head;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qb[qt][kk] = as_bf16x8(ld16(qp + 16 * kk + 8 * kg));
+static int prefill_grid() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cache[dev]) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_score_kernel<true>, kPfThreads, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    cache[dev] = device_cus() * per_cu;
   }
-  // smallest / largest position among this wave's rows (rows are position-ordered)
-  const int wave_row0 = row0 + 64 * wave;
-  const int wave_pos_min = seq - Q + min(wave_row0, HQ - 1) / H;
-  const int wave_pos_max = seq - Q + min(wave_row0 + 63, HQ - 1) / H;
-  const bool wave_live = wave_row0 < HQ;
-  const int32_t* bt_row = a.bt + (int64_t)r * a.bt_stride;
-
-  auto compute = [&](const uint8_t* kl, int b) {
-    if (!(wave_live && wave_pos_max >= kBlock * b)) return;
-    const bool full = kBlock * b + (kBlock - 1) <= wave_pos_min;
-    float m[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int tok = 32 * tt + nl;
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(&kl[swz(tok, 2 * kk + kg)]));
-        acc[0] = mfma32(ka, qb[0][kk], acc[0]);
-        acc[1] = mfma32(ka, qb[1][kk], acc[1]);
-      }
-      // acc[qt][i]: token 32*tt + 8*(i/4) + 4*kg + i%4 against row nl of tile qt
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        if (full) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) m[qt] = fmaxf(m[qt], acc[qt][i]);
-        } else {
-          const int lim = pos_q[qt] - kBlock * b;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * tt + 8 * (i >> 2) + 4 * kg + (i & 3) <= lim) m[qt] = fmaxf(m[qt], acc[qt][i]);
-        }
-      }
-    }
-    m[0] = wave_max_xor(m[0], 32);
-    m[1] = wave_max_xor(m[1], 32);
-    // lanes 0..31 stage tile 0's rows, lanes 32..63 tile 1's
-    const float v = kg ? m[1] : m[0];
-    const int srow = 64 * wave + 32 * kg + nl;
-    sstage[srow * kPrefillBlocksPerSplit + ((b - b_begin) ^ (srow & 15))] = v * a.sm_scale;
-  };
-
-  dma_page(kl0, a.kdata, bt_row[b_begin], wave, lane);
-  __syncthreads();
-  for (int b = b_begin; b < b_end; b += 2) {
-    if (b + 1 < b_end) dma_page(kl1, a.kdata, bt_row[b + 1], wave, lane);
-    compute(kl0, b);
-    __syncthreads();  // also waits for the copy into kl1
-    if (b + 1 < b_end) {
-      if (b + 2 < b_end) dma_page(kl0, a.kdata, bt_row[b + 2], wave, lane);
-      compute(kl1, b + 1);
-      __syncthreads();
-    }
-  }
-  // Write the staged scores: 16 consecutive blocks of a row per 16 lanes.
-  // Only visible (row, block) entries are written.
-  const int nbl = b_end - b_begin;
-  for (int k = 0; k < kPrefillRows * kPrefillBlocksPerSplit / 256; ++k) {
-    const int e = 256 * k + threadIdx.x;
-    const int row = e / kPrefillBlocksPerSplit, j = e % kPrefillBlocksPerSplit;
-    const int i = row0 + row;
-    if (j < nbl && i < HQ) {
-      const int jq = i / H, h = i - jq * H;
-      const int pos = seq - Q + jq;
-      const int b = b_begin + j;
-      if (pos >= kBlock * b)
-        a.scores[(int64_t)h * a.s_head + (int64_t)(r * Q + jq) * a.s_row + b] =
-            sstage[row * kPrefillBlocksPerSplit + (j ^ (row & 15))];
-    }
-  }
+  return cache[dev];
 }
 
 hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s) {
-  const int row_tiles = (a.heads * a.qlen + kPrefillRows - 1) / kPrefillRows;
-  const int splits = (a.nb_max + kPrefillBlocksPerSplit - 1) / kPrefillBlocksPerSplit;
-  hipLaunchKernelGGL(prefill_score_kernel, dim3(row_tiles, a.num_reqs, splits), dim3(256), 0, s, a);
+  const int tiles = (a.heads * a.qlen + kPrefillRows - 1) / kPrefillRows;
+  const int64_t units = (int64_t)a.num_reqs * tiles;
+  // the scan counts steps in 32-bit integers
+  if (units <= kPfBalancedMaxUnits && units * a.nb_max <= INT32_MAX) {
+    hipLaunchKernelGGL(prefill_score_kernel<true>, dim3(prefill_grid()), dim3(kPfThreads), 0, s, a, (int)units,
+                       tiles);
+  } else {
+    hipLaunchKernelGGL(prefill_score_kernel<false>, dim3((unsigned)units), dim3(kPfThreads), 0, s, a, (int)units,
+                       tiles);
+  }
   return hipGetLastError();
 }
 

@@ -94,6 +94,8 @@ BAD_PROBLEMS = [
     ("q_head_overlap", dict(q_head_stride=64), "head stride"),
     ("table_narrow", dict(bt_width=63), "narrower"),
     ("table_row_stride", dict(bt_row_stride=32), "row stride"),
+    ("tokens_overflow", dict(num_reqs=1 << 20, query_len=1 << 12), "2^31"),
+    ("rows_overflow", dict(heads=1 << 16, query_len=1 << 16, q_head_stride=128), "2^31"),
 ]
 
 

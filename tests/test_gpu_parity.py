@@ -177,6 +177,14 @@ EDGE = [
     ("generic_selector_long", dict(R=2, lens=(140000, 160000), Q=1, H=1, max_seq_len=163840,
                                    topk=16, I=1, L=2)),
     ("prefill_h1_ragged", dict(R=2, lens=(300, 2000), Q=300, H=1, max_seq_len=2048, topk=8, I=1, L=1)),
+    # prefill scorer: workgroup shares that start and end inside row tiles,
+    # cross into the next tile and request, and a last tile of 8 rows
+    ("prefill_many_tiles_mixed", dict(R=12, lens=(100, 5000), Q=700, H=4, max_seq_len=8192, topk=16,
+                                      I=1, L=2)),
+    ("prefill_h8_tail_tile", dict(R=3, lens=(1000, 3000), Q=65, H=8, max_seq_len=4096, topk=8, I=1, L=1)),
+    # tiles whose rows all sit before the first key (no steps) between live ones
+    ("prefill_seq_shorter_than_q", dict(R=4, lens=(0, 0), Q=600, H=1, max_seq_len=1024, topk=4, I=1, L=1,
+                                        fixed_lens=[100, 700, 0, 1])),
 ]
 
 
@@ -295,6 +303,25 @@ def test_full_size_prefill():
         near = P.check_ids(out[:, rows].cpu().numpy(), ids_ref, s_ref, a["seq_lens"], w.query_len,
                            w.topk, w.init_blocks, w.local_blocks, rows=loc)
         _say(f"full config 4 req {r}: {len(loc)} sampled rows, max err {err:.3g}, near-tie rows {near}")
+
+
+def test_prefill_one_workgroup_per_tile_grid():
+    """More (request, row tile) units than the balanced prefill grid scans:
+    one workgroup per tile.  Sampled requests against the oracle, the
+    selection invariants on every row."""
+    w = make(name="many_tiles", R=65600, lens=(1, 128), Q=17, H=1, max_seq_len=128, topk=1, I=0, L=0,
+             kfmt=KFMT_BF16, seed=11, device=DEV)
+    _say(f"prefill per-tile grid: R={w.num_reqs} Q={w.query_len}")
+    scores, out = run_split(w)
+    P.check_invariants(out.cpu().numpy(), w.seq_lens.cpu().numpy(), w.query_len, w.topk,
+                       w.init_blocks, w.local_blocks)
+    reqs = [0, 1, 40000, 65599]
+    a, rows = host_subset(w, reqs)
+    s_ref, ids_ref = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
+    err = P.check_scores(scores[:, rows].cpu().numpy(), s_ref)
+    near = P.check_ids(out[:, rows].cpu().numpy(), ids_ref, s_ref, a["seq_lens"], w.query_len,
+                       w.topk, w.init_blocks, w.local_blocks)
+    _say(f"prefill per-tile grid: sampled reqs {reqs}: max err {err:.3g}, near-tie rows {near}")
 
 
 def test_sparse_block_table_matches_oracle():
