@@ -107,14 +107,24 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t x, u32x2 tab) {
 // ------------------------------------------------------------------ scorer
 
 // A wave scores one block (page) as two halves of 64 tokens.  Half h of the
-// page is held as 4 token tiles x 4 k-steps of MFMA A operands (bf16), or as
-// 4 tiles of 16 nibble bytes plus their 2 scale bytes (NVFP4).
+// page is held as the 16 contiguous KiB it spans, one 16-byte piece per lane
+// and load (bf16), or as 4 tiles of 16 nibble bytes plus their 2 scale bytes
+// (NVFP4).
 template <int KFMT>
 struct HalfBuf;
 template <>
 struct HalfBuf<0> {
-  u32x4 v[4][4];
+  u32x4 v[16];
 };
+
+// Cache policy of the key loads: non-temporal (each key is read once per
+// pass; streaming it past the caches is worth ~12% of bandwidth with whole
+// 1 KiB runs per load instruction).
+constexpr int kKeyLoadPolicy = 2;
+
+// bf16 half pages reach the MFMA operand layout through a per-wave 8 KiB
+// LDS area, a quarter page (32 tokens x 256 B) at a time.
+constexpr int kTransposeBytes = 32 * kDim * 2;
 template <>
 struct HalfBuf<1> {
   u32x4 nib[4];
@@ -202,25 +212,28 @@ __device__ __forceinline__ void set_q(QRows& q, const QRaw& raw, const ScoreArgs
 // live == false issues the same instructions with an empty descriptor: they
 // return zeros and move no data, which keeps the loop free of branches
 // around loads (and the wait counts exact).
+//   bf16: load i reads KiB i of the half: lane l takes token 4i + l/16 of the
+//   half, 16-byte chunk l%16 (whole 128-byte lines per instruction).
+//   NVFP4: load tt reads tokens 16tt + l%16 of the half, nibble bytes
+//   16(l/16).. (again one contiguous KiB), plus their 2 scale bytes.
 template <int KFMT>
 __device__ __forceinline__ void issue_half(HalfBuf<KFMT>& buf, const ScoreArgs& a, int64_t page,
                                            int half, int n, int g, bool live) {
   if constexpr (KFMT == 0) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(a.kdata + page * (kBlock * kDim * 2), live ? kBlock * kDim * 2 : 0);
-    const int voff = n * (kDim * 2) + 16 * g;
+    const int voff = 16 * (16 * g + n);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        buf.v[tt][kc] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * kc, (4 * half + tt) * 4096, 0));
+    for (int i = 0; i < 16; ++i)
+      buf.v[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, half * 16384 + i * 1024, kKeyLoadPolicy));
   } else {
     const __amdgpu_buffer_rsrc_t rn = rsrc(a.kdata + page * (kBlock * kDim / 2), live ? kBlock * kDim / 2 : 0);
     const __amdgpu_buffer_rsrc_t rsc = rsrc(a.kscales + page * (kBlock * kDim / 16), live ? kBlock * kDim / 16 : 0);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       buf.nib[tt] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, n * (kDim / 2) + 16 * g, (4 * half + tt) * 1024, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, n * (kDim / 2) + 16 * g, (4 * half + tt) * 1024,
+                                                       kKeyLoadPolicy));
       buf.sc[tt] = __builtin_amdgcn_raw_buffer_load_b16(rsc, n * (kDim / 16) + 2 * g, (4 * half + tt) * 128, 0);
     }
   }
@@ -229,30 +242,61 @@ __device__ __forceinline__ void issue_half(HalfBuf<KFMT>& buf, const ScoreArgs& 
 // Multiply half `half` of a page by the query rows and fold its tokens into
 // this lane's running maximum m (lane l: row l%16, tokens 4*(l/16) + 0..3 of
 // each 16-token tile).  lim: token s of the block is visible iff s <= lim.
+// bf16: each quarter (32 tokens) is written to the wave's LDS area tb as
+// loaded -- token t's 16-byte chunk c at slot c ^ (t & 15) of its 256-byte
+// row -- and read back as MFMA A operands (token 16tt + l%16, chunk
+// 4kc + l/16); the XOR keeps both the writes (8 chunks of one token) and the
+// reads (one chunk of 8 tokens) free of bank conflicts.
 template <int KFMT>
 __device__ __forceinline__ void compute_half(const HalfBuf<KFMT>& buf, const QRows& q, const u32x2* lut,
-                                             int half, bool full, int lim, int g, float& m) {
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (KFMT == 0) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(buf.v[tt][kc]), q.qb[kc], acc);
+                                             uint8_t* tb, int half, bool full, int lim, int n, int g,
+                                             float& m) {
+  auto fold = [&](const f32x4& acc, int s0) {
+    if (full) {
+      m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
     } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s0 + i <= lim) m = fmaxf(m, acc[i]);
+    }
+  };
+  if constexpr (KFMT == 0) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      // the wave's lanes exchange data through tb: keep the compiler from
+      // moving these writes above the previous quarter's reads, or the
+      // reads below above these writes (it only sees each lane's own
+      // addresses; the hardware keeps one wave's LDS accesses in order)
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 4 * j + g;
+        *reinterpret_cast<u32x4*>(tb + t * (kDim * 2) + ((n ^ (t & 15)) << 4)) = buf.v[8 * qq + j];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 16 * tt + n;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(tb + t * (kDim * 2) + (((4 * kc + g) ^ n) << 4));
+          acc = mfma16(as_bf16x8(v), q.qb[kc], acc);
+        }
+        fold(acc, 64 * half + 32 * qq + 16 * tt + 4 * g);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       const u32x2 t0 = lut[buf.sc[tt] & 0xFF];
       const u32x2 t1 = lut[(buf.sc[tt] >> 8) & 0xFF];
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].x, t0)), q.qb[0], acc);
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].y, t0)), q.qb[1], acc);
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].z, t1)), q.qb[2], acc);
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].w, t1)), q.qb[3], acc);
-    }
-    if (full) {
-      m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-    } else {
-      const int s0 = 64 * half + 16 * tt + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (s0 + i <= lim) m = fmaxf(m, acc[i]);
+      fold(acc, 64 * half + 16 * tt + 4 * g);
     }
   }
 }
@@ -302,8 +346,8 @@ __device__ __forceinline__ void flush_scores(const __amdgpu_buffer_rsrc_t& srs, 
 // around a load and the wait counts stay exact.  STAGED == false (score
 // tensors past 2 GiB) stores each value directly.
 template <int KFMT, bool STAGED, typename Walk>
-__device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut, Walk& walk, float* stv,
-                                           int32_t* sto) {
+__device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut, uint8_t* tb, Walk& walk,
+                                           float* stv, int32_t* sto) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int HQ = a.heads * a.qlen;
   const int stage_blocks = kStage / HQ;
@@ -327,12 +371,12 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut,
     const bool full = kBlock * cur.b + (kBlock - 1) <= cur.seq - a.qlen;
     const int lim = q.pos - kBlock * cur.b;
     float m = -INFINITY;
-    compute_half<KFMT>(A, q, lut, 0, full, lim, g, m);
+    compute_half<KFMT>(A, q, lut, tb, 0, full, lim, n, g, m);
     __builtin_amdgcn_sched_barrier(0);
     const QRaw qn = issue_q<KFMT>(a, nxt.r, n, g, new_req);
     issue_half<KFMT>(A, a, nxt.page, 0, n, g, has_next);
     __builtin_amdgcn_sched_barrier(0);
-    compute_half<KFMT>(B, q, lut, 1, full, lim, g, m);
+    compute_half<KFMT>(B, q, lut, tb, 1, full, lim, n, g, m);
     __builtin_amdgcn_sched_barrier(0);
     issue_half<KFMT>(B, a, nxt.page, 1, n, g, has_next);
     __builtin_amdgcn_sched_barrier(0);
@@ -417,6 +461,7 @@ __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
   __shared__ int32_t part[256];
   __shared__ float stage_v[4][kStage];
   __shared__ int32_t stage_o[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[4][KFMT == 0 ? kTransposeBytes : 16];
   const int R = a.num_reqs;
   int32_t* pre = smem;        // [R + 1]
   int32_t* sl = smem + R + 1;  // [R]
@@ -453,259 +498,7 @@ __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
   // of a row (and their score writes) stay with one wave
   const int64_t span = hi - lo;
   BalancedWalk walk{&a, pre, sl, lo + span * wave / 4, lo + span * (wave + 1) / 4};
-  score_wave<KFMT, true>(a, lut, walk, stage_v[wave], stage_o[wave]);
-}
-
-// ---- workgroup-cooperative scorer
-//
-// The four waves of a workgroup score every block of the workgroup's slice
-// together: wave w multiplies tokens [32w, 32w+32) and the four partial
-// maxima meet in LDS (one barrier per block).  Balance is thus set per
-// workgroup (slices differ by at most one block), not per wave, and each
-// wave keeps a ring of kRing quarter-pages in flight.  A request change is
-// seen kRing blocks ahead: the new query rows are loaded with that block's
-// pages, so switching requests does not drain the ring.
-
-template <int KFMT>
-struct QuarterBuf;
-template <>
-struct QuarterBuf<0> {
-  u32x4 v[2][4];
-};
-template <>
-struct QuarterBuf<1> {
-  u32x4 nib[2];
-  uint32_t sc[2];
-};
-
-template <int KFMT>
-constexpr int kRing = KFMT == 0 ? 4 : 8;
-
-template <int KFMT>
-__device__ __forceinline__ void issue_quarter(QuarterBuf<KFMT>& buf, const ScoreArgs& a, int64_t page,
-                                              int w, int n, int g, bool live) {
-  if constexpr (KFMT == 0) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(a.kdata + page * (kBlock * kDim * 2), live ? kBlock * kDim * 2 : 0);
-    const int voff = n * (kDim * 2) + 16 * g;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        buf.v[tt][kc] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * kc, (2 * w + tt) * 4096, 0));
-  } else {
-    const __amdgpu_buffer_rsrc_t rn = rsrc(a.kdata + page * (kBlock * kDim / 2), live ? kBlock * kDim / 2 : 0);
-    const __amdgpu_buffer_rsrc_t rsc = rsrc(a.kscales + page * (kBlock * kDim / 16), live ? kBlock * kDim / 16 : 0);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      buf.nib[tt] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, n * (kDim / 2) + 16 * g, (2 * w + tt) * 1024, 0));
-      buf.sc[tt] = __builtin_amdgcn_raw_buffer_load_b16(rsc, n * (kDim / 16) + 2 * g, (2 * w + tt) * 128, 0);
-    }
-  }
-}
-
-template <int KFMT>
-__device__ __forceinline__ void compute_quarter(const QuarterBuf<KFMT>& buf, const QRows& q, const u32x2* lut,
-                                                int w, bool full, int lim, int g, float& m) {
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (KFMT == 0) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) acc = mfma16(as_bf16x8(buf.v[tt][kc]), q.qb[kc], acc);
-    } else {
-      const u32x2 t0 = lut[buf.sc[tt] & 0xFF];
-      const u32x2 t1 = lut[(buf.sc[tt] >> 8) & 0xFF];
-      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].x, t0)), q.qb[0], acc);
-      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].y, t0)), q.qb[1], acc);
-      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].z, t1)), q.qb[2], acc);
-      acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].w, t1)), q.qb[3], acc);
-    }
-    if (full) {
-      m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-    } else {
-      const int s0 = 32 * w + 16 * tt + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (s0 + i <= lim) m = fmaxf(m, acc[i]);
-    }
-  }
-}
-
-// Block sequence of one workgroup (identical in all its waves).
-struct CoopWalk {
-  const ScoreArgs* a;
-  const int32_t* pre;
-  const int32_t* sl;
-  int64_t gb, hi;
-  int r;
-
-  __device__ __forceinline__ bool next(Cur& c) {
-    if (gb >= hi) {
-      c.r = r;
-      c.b = 0;
-      c.seq = 0;
-      c.page = 0;
-      return false;
-    }
-    int rr = r;
-    while (pre[rr + 1] <= gb) ++rr;
-    r = __builtin_amdgcn_readfirstlane(rr);
-    c.r = r;
-    c.b = __builtin_amdgcn_readfirstlane((int)(gb - pre[r]));
-    c.seq = __builtin_amdgcn_readfirstlane(sl[r]);
-    __builtin_amdgcn_sched_barrier(0);
-    c.page = page_of(*a, c.r, c.b);
-    ++gb;
-    return true;
-  }
-};
-
-// Query rows of up to kQCache requests staged in LDS per epoch: [request]
-// [row n][16-byte chunk c ^ n] (the XOR keeps the 16 lanes that read one
-// chunk of 16 rows on distinct banks).
-constexpr int kQCache = 8;
-
-// Stage the rows of requests r0 .. r0+nq-1 (thread t moves chunk t%16 of
-// row t/16; rows past H*Q are zero).
-__device__ __forceinline__ void stage_q(uint32_t* qc, const ScoreArgs& a, int r0, int nq) {
-  const int H = a.heads, Q = a.qlen;
-  const int n = threadIdx.x >> 4, c = threadIdx.x & 15;
-  for (int i = 0; i < nq; ++i) {
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (n < H * Q) {
-      const int j = n / H, h = n - (n / H) * H;
-      v = ld16(a.q + ((int64_t)(r0 + i) * Q + j) * a.q_tok + (int64_t)h * a.q_head + 8 * c);
-    }
-    *reinterpret_cast<u32x4*>(qc + ((i * 16 + n) * 16 + (c ^ n)) * 4) = v;
-  }
-}
-
-// This lane's query operands of cached request slot i (see issue_q for the
-// element order).
-template <int KFMT>
-__device__ __forceinline__ QRaw read_q(const uint32_t* qc, int i, int n, int g) {
-  QRaw q;
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    const int d = KFMT == 0 ? 32 * kc + 8 * g : 32 * g + 8 * kc;
-    const int c = d >> 3;
-    q.v[kc] = *reinterpret_cast<const u32x4*>(qc + ((i * 16 + n) * 16 + (c ^ n)) * 4);
-  }
-  return q;
-}
-
-template <int KFMT>
-__global__ __launch_bounds__(256) void decode_score_coop(ScoreArgs a) {
-  extern __shared__ int32_t smem[];
-  __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
-  __shared__ int32_t part[256];
-  __shared__ float red[2][4][16];
-  __shared__ __attribute__((aligned(16))) uint32_t qc[kQCache * 16 * 16 * 4];
-  const int R = a.num_reqs;
-  int32_t* pre = smem;         // [R + 1]
-  int32_t* sl = smem + R + 1;  // [R]
-  const int per = (R + 255) / 256;
-  const int r0 = min(R, (int)threadIdx.x * per), r1 = min(R, r0 + per);
-  int sum = 0;
-  for (int r = r0; r < r1; ++r) {
-    const int s = a.seq_lens[r];
-    sl[r] = s;
-    sum += s > 0 ? (s - 1) / kBlock + 1 : 0;
-  }
-  part[threadIdx.x] = sum;
-  if constexpr (KFMT == 1) fill_lut(lut);
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int base = threadIdx.x ? part[threadIdx.x - 1] : 0;
-  for (int r = r0; r < r1; ++r) {
-    pre[r] = base;
-    const int s = sl[r];
-    base += s > 0 ? (s - 1) / kBlock + 1 : 0;
-  }
-  if (threadIdx.x == 255) pre[R] = part[255];
-  __syncthreads();
-  const int64_t total = pre[R];
-  const int64_t lo = total * blockIdx.x / gridDim.x;
-  const int64_t hi = total * (blockIdx.x + 1) / gridDim.x;
-
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int HQ = a.heads * a.qlen;
-  constexpr int D = kRing<KFMT>;
-  // score stores go through a descriptor over the whole score tensor; a
-  // lane that must not write uses an offset past its end
-  const __amdgpu_buffer_rsrc_t srs = rsrc(a.scores, a.s_bytes);
-
-  int64_t e_lo = lo;
-  while (e_lo < hi) {  // epochs: at most kQCache requests each
-    int rq0;
-    {
-      int l = 0, u = R;  // last r with pre[r] <= e_lo
-      while (u - l > 1) {
-        const int mid = (l + u) >> 1;
-        if (pre[mid] <= e_lo) l = mid; else u = mid;
-      }
-      rq0 = __builtin_amdgcn_readfirstlane(l);
-    }
-    const int rq_end = min(R, rq0 + kQCache);
-    const int64_t e_hi = min(hi, (int64_t)pre[rq_end]);
-    stage_q(qc, a, rq0, rq_end - rq0);
-    __syncthreads();
-
-    CoopWalk walk{&a, pre, sl, e_lo, e_hi, rq0};
-    Cur c[D];
-    bool live[D];
-    QuarterBuf<KFMT> buf[D];
-#pragma unroll
-    for (int k = 0; k < D; ++k) {
-      live[k] = walk.next(c[k]);
-      issue_quarter<KFMT>(buf[k], a, c[k].page, w, n, g, live[k]);
-    }
-    QRows q;
-    int q_r = -1;
-    // whole rounds of the ring, no early exit: slots past the end compute on
-    // zeros and store nothing, which keeps this a simple counted loop
-    const int rounds = (int)((e_hi - e_lo + D - 1) / D);
-    for (int rd = 0; rd < rounds; ++rd) {
-#pragma unroll
-      for (int k = 0; k < D; ++k) {
-        const Cur cur = c[k];
-        const bool cur_live = live[k];
-        if (cur.r != q_r) {
-          set_q<KFMT>(q, read_q<KFMT>(qc, cur.r - rq0, n, g), a, cur.r, cur.seq, n);
-          q_r = cur.r;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const bool full = kBlock * cur.b + (kBlock - 1) <= cur.seq - a.qlen;
-        const int lim = q.pos - kBlock * cur.b;
-        float m = -INFINITY;
-        compute_quarter<KFMT>(buf[k], q, lut, w, full, lim, g, m);
-        __builtin_amdgcn_sched_barrier(0);
-        live[k] = walk.next(c[k]);  // refill this slot with the block kRing ahead
-        issue_quarter<KFMT>(buf[k], a, c[k].page, w, n, g, live[k]);
-        __builtin_amdgcn_sched_barrier(0);
-        m = wave_max_xor(m, 16);
-        m = wave_max_xor(m, 32);
-        if (g == 0) red[k & 1][w][n] = m;
-        __syncthreads();
-        const float v = fmaxf(fmaxf(red[k & 1][0][n], red[k & 1][1][n]),
-                              fmaxf(red[k & 1][2][n], red[k & 1][3][n]));
-        const bool writer = cur_live && w == 0 && g == 0 && n < HQ && q.pos >= kBlock * cur.b;
-        const int off = writer ? (int)(((int64_t)q.h * a.s_head + (int64_t)q.t * a.s_row + cur.b) * 4)
-                               : 0x7FFFFFF0;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v * a.sm_scale), srs, off, 0, 0);
-      }
-    }
-    __syncthreads();  // the next epoch restages the query cache
-    e_lo = e_hi;
-  }
+  score_wave<KFMT, true>(a, lut, tbuf[wave], walk, stage_v[wave], stage_o[wave]);
 }
 
 // ---- per-request chunk scorer (any batch size)
@@ -737,6 +530,7 @@ struct ChunkWalk {
 template <int KFMT>
 __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
   __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[4][KFMT == 0 ? kTransposeBytes : 16];
   const int r = blockIdx.y;
   const int seq = a.seq_lens[r];
   if (seq <= 0) return;
@@ -749,12 +543,12 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
   }
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   ChunkWalk walk{&a, r, seq, b_begin + wave, min(nb, b_begin + a.blocks_per_wg)};
-  score_wave<KFMT, false>(a, lut, walk, nullptr, nullptr);
+  score_wave<KFMT, false>(a, lut, tbuf[wave], walk, nullptr, nullptr);
 }
 
 // ------------------------------------------------------------------ launch
 
-// Largest batch whose lengths and prefix sums fit the cooperative scorer's LDS.
+// Largest batch whose lengths and prefix sums fit the balanced scorer's LDS.
 constexpr int kBalancedMaxReqs = 8192;
 
 int device_cus() {
@@ -769,7 +563,7 @@ int device_cus() {
   return cache[dev];
 }
 
-// Workgroups of the cooperative scorer resident per CU with `lds` bytes of
+// Workgroups of the balanced scorer resident per CU with `lds` bytes of
 // dynamic LDS (cached per 1 KiB step of LDS).
 template <int KFMT>
 static int balanced_occupancy(size_t lds) {
@@ -786,32 +580,9 @@ static int balanced_occupancy(size_t lds) {
 }
 
 template <int KFMT>
-static int coop_occupancy(size_t lds) {
-  static int cache[(2 * kBalancedMaxReqs + 1) * 4 / 1024 + 2] = {0};
-  const size_t key = (lds + 1023) / 1024;
-  if (!cache[key]) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_score_coop<KFMT>, 256, key * 1024) != hipSuccess ||
-        v <= 0)
-      v = 1;
-    cache[key] = v;
-  }
-  return cache[key];
-}
-
-#ifndef MM3_DECODE_SCHED
-#define MM3_DECODE_SCHED 0
-#endif
-// 0: per-wave length-balanced scorer, 1: workgroup-cooperative scorer
-constexpr int kDecodeSched = MM3_DECODE_SCHED;
-
-template <int KFMT>
 static hipError_t launch_decode(const ScoreArgs& a, hipStream_t s) {
   const size_t lds = (size_t)(2 * a.num_reqs + 1) * sizeof(int32_t);
-  if (kDecodeSched == 1 && a.num_reqs <= kBalancedMaxReqs && a.s_bytes > 0) {
-    const int grid = device_cus() * coop_occupancy<KFMT>(lds);
-    hipLaunchKernelGGL(decode_score_coop<KFMT>, dim3(grid), dim3(256), lds, s, a);
-  } else if (kDecodeSched == 0 && a.num_reqs <= kBalancedMaxReqs && a.s_bytes > 0) {
+  if (a.num_reqs <= kBalancedMaxReqs && a.s_bytes > 0) {
     const int grid = device_cus() * balanced_occupancy<KFMT>(lds);
     hipLaunchKernelGGL(decode_score_balanced<KFMT>, dim3(grid), dim3(256), lds, s, a);
   } else {
