@@ -22,6 +22,15 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source additions.  decode_score: max() without NaN canonicalisation
+# (block scores of rows whose q or keys hold NaN are unspecified) and MFMA
+# results in ordinary VGPRs (no accumulator-register reads per tile); together
+# they take ~8% of the vector instructions out of the NVFP4 scorer's loop.
+SOURCE_FLAGS = {
+    "decode_score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -42,7 +51,8 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE, "-I", CSRC,
+               "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

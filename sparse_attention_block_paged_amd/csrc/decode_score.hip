@@ -128,7 +128,7 @@ constexpr int kTransposeBytes = 32 * kDim * 2;
 template <>
 struct HalfBuf<1> {
   u32x4 nib[4];
-  uint32_t sc[4];
+  u32x2 scl;  // the 8 scale bytes of token l of the half (lane l)
 };
 
 struct QRows {
@@ -215,7 +215,9 @@ __device__ __forceinline__ void set_q(QRows& q, const QRaw& raw, const ScoreArgs
 //   bf16: load i reads KiB i of the half: lane l takes token 4i + l/16 of the
 //   half, 16-byte chunk l%16 (whole 128-byte lines per instruction).
 //   NVFP4: load tt reads tokens 16tt + l%16 of the half, nibble bytes
-//   16(l/16).. (again one contiguous KiB), plus their 2 scale bytes.
+//   16(l/16).. (again one contiguous KiB); one more load brings the half's
+//   512 scale bytes, token l's 8 to lane l (the multiply fetches the pair
+//   it needs from that lane).
 template <int KFMT>
 __device__ __forceinline__ void issue_half(HalfBuf<KFMT>& buf, const ScoreArgs& a, int64_t page,
                                            int half, int n, int g, bool live) {
@@ -230,12 +232,13 @@ __device__ __forceinline__ void issue_half(HalfBuf<KFMT>& buf, const ScoreArgs& 
     const __amdgpu_buffer_rsrc_t rn = rsrc(a.kdata + page * (kBlock * kDim / 2), live ? kBlock * kDim / 2 : 0);
     const __amdgpu_buffer_rsrc_t rsc = rsrc(a.kscales + page * (kBlock * kDim / 16), live ? kBlock * kDim / 16 : 0);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 4; ++tt)
       buf.nib[tt] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, n * (kDim / 2) + 16 * g, (4 * half + tt) * 1024,
                                                        kKeyLoadPolicy));
-      buf.sc[tt] = __builtin_amdgcn_raw_buffer_load_b16(rsc, n * (kDim / 16) + 2 * g, (4 * half + tt) * 128, 0);
-    }
+    buf.scl = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsc, 8 * (16 * g + n), half * 512,
+                                                    kKeyLoadPolicy));
   }
 }
 
@@ -289,9 +292,15 @@ __device__ __forceinline__ void compute_half(const HalfBuf<KFMT>& buf, const QRo
   } else {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
+      // scale bytes 2g, 2g+1 (dims [32g, 32g+32)) of token 16tt + n, held by
+      // lane 16tt + n
+      const int src = (16 * tt + n) * 4;
+      const uint32_t wx = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)buf.scl.x);
+      const uint32_t wy = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)buf.scl.y);
+      const uint32_t sc = ((g < 2 ? wx : wy) >> (16 * (g & 1))) & 0xFFFFu;
+      const u32x2 t0 = lut[sc & 0xFF];
+      const u32x2 t1 = lut[sc >> 8];
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      const u32x2 t0 = lut[buf.sc[tt] & 0xFF];
-      const u32x2 t1 = lut[(buf.sc[tt] >> 8) & 0xFF];
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].x, t0)), q.qb[0], acc);
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].y, t0)), q.qb[1], acc);
       acc = mfma16(as_bf16x8(fp4x8_to_bf16(buf.nib[tt].z, t1)), q.qb[2], acc);
@@ -338,68 +347,121 @@ __device__ __forceinline__ void flush_scores(const __amdgpu_buffer_rsrc_t& srs, 
   }
 }
 
-// Score every block the walker hands this wave.  Loads run one block ahead:
-// while half 0 of block i is multiplied, half 1 of block i is in flight;
-// while half 1 is multiplied, the next block's query rows (on a request
-// change) and its half 0 are.  Loads are issued unconditionally (empty
-// descriptors where there is nothing to fetch), so the loop has no branch
-// around a load and the wait counts stay exact.  STAGED == false (score
-// tensors past 2 GiB) stores each value directly.
+// Blocks whose loads a wave keeps in flight besides the one it multiplies:
+// one (its second half in flight while the first is multiplied, the next
+// block's first half while the second is).  bf16 half pages take 64
+// registers, so that is all that fits; NVFP4 half pages take 18, but a
+// deeper ring costs waves per SIMD, and the NVFP4 scorer is bound by its
+// decode more than by loads in flight (2 and 3 blocks measured slower).
+#ifndef MM3_FP4_RING
+#define MM3_FP4_RING 1
+#endif
+template <int KFMT>
+constexpr int kRingBlocks = KFMT == 0 ? 1 : MM3_FP4_RING;
+
+// One block of the ring: the walker's position, whether it is real, its two
+// half pages, and the query loads of its request when that request differs
+// from the previous block's.
+template <int KFMT>
+struct RingBlock {
+  Cur c;
+  bool live;
+  bool new_req;
+  QRaw qraw;
+  HalfBuf<KFMT> h0, h1;
+};
+
+// Score every block the walker hands this wave, in order.  Block i's loads
+// are issued when block i - kRingBlocks is multiplied (its first half after
+// that block's first half, its second half after the second), so the wave
+// always has about kRingBlocks blocks of keys in flight.  A block that starts
+// a new request also brings that request's query rows, loaded with its pages.
+// Loads are issued unconditionally (empty descriptors where there is nothing
+// to fetch), so the loop has no branch around a load and the wait counts
+// stay exact.  STAGED == false (score tensors past 2 GiB) stores each value
+// directly.
 template <int KFMT, bool STAGED, typename Walk>
 __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut, uint8_t* tb, Walk& walk,
                                            float* stv, int32_t* sto) {
+  constexpr int DB = kRingBlocks<KFMT>;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int HQ = a.heads * a.qlen;
   const int stage_blocks = kStage / HQ;
-  Cur cur;
-  if (!walk.first(cur)) return;
+  RingBlock<KFMT> ring[DB];
+  if (!walk.first(ring[0].c)) return;
   QRows q;
   {
-    const QRaw raw = issue_q<KFMT>(a, cur.r, n, g, true);
-    set_q<KFMT>(q, raw, a, cur.r, cur.seq, n);
+    const QRaw raw = issue_q<KFMT>(a, ring[0].c.r, n, g, true);
+    set_q<KFMT>(q, raw, a, ring[0].c.r, ring[0].c.seq, n);
   }
-  HalfBuf<KFMT> A, B;
-  issue_half<KFMT>(A, a, cur.page, 0, n, g, true);
-  issue_half<KFMT>(B, a, cur.page, 1, n, g, true);
+  ring[0].live = true;
+  ring[0].new_req = false;
+  issue_half<KFMT>(ring[0].h0, a, ring[0].c.page, 0, n, g, true);
+  issue_half<KFMT>(ring[0].h1, a, ring[0].c.page, 1, n, g, true);
+  Cur last = ring[0].c;  // the last block issued (the walker's position)
+  bool more = true;      // the walker has not run out
+#pragma unroll
+  for (int j = 1; j < DB; ++j) {
+    RingBlock<KFMT>& rb = ring[j];
+    rb.c = last;
+    rb.live = more && walk.next(rb.c);
+    more = rb.live;
+    rb.new_req = rb.live && rb.c.r != last.r;
+    rb.qraw = issue_q<KFMT>(a, rb.c.r, n, g, rb.new_req);
+    issue_half<KFMT>(rb.h0, a, rb.c.page, 0, n, g, rb.live);
+    issue_half<KFMT>(rb.h1, a, rb.c.page, 1, n, g, rb.live);
+    if (rb.live) last = rb.c;
+  }
   const __amdgpu_buffer_rsrc_t srs = rsrc(a.scores, STAGED ? a.s_bytes : 0);
   int staged = 0;  // blocks in the stage (wave-uniform)
   while (true) {
-    Cur nxt = cur;
-    const bool has_next = walk.next(nxt);
-    const bool new_req = has_next && nxt.r != cur.r;
-    __builtin_amdgcn_sched_barrier(0);
-    const bool full = kBlock * cur.b + (kBlock - 1) <= cur.seq - a.qlen;
-    const int lim = q.pos - kBlock * cur.b;
-    float m = -INFINITY;
-    compute_half<KFMT>(A, q, lut, tb, 0, full, lim, n, g, m);
-    __builtin_amdgcn_sched_barrier(0);
-    const QRaw qn = issue_q<KFMT>(a, nxt.r, n, g, new_req);
-    issue_half<KFMT>(A, a, nxt.page, 0, n, g, has_next);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_half<KFMT>(B, q, lut, tb, 1, full, lim, n, g, m);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_half<KFMT>(B, a, nxt.page, 1, n, g, has_next);
-    __builtin_amdgcn_sched_barrier(0);
-    m = wave_max_xor(m, 16);
-    m = wave_max_xor(m, 32);
-    const bool writer = n < HQ && q.pos >= kBlock * cur.b;
-    const int64_t off = (int64_t)q.h * a.s_head + (int64_t)q.t * a.s_row + cur.b;
-    if constexpr (STAGED) {
-      if (g == 0 && n < HQ) {
-        stv[staged * HQ + n] = m * a.sm_scale;
-        sto[staged * HQ + n] = writer ? (int32_t)(off * 4) : 0x7FFFFFF0;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      RingBlock<KFMT>& rb = ring[j];
+      if (!rb.live) goto done;
+      const Cur cur = rb.c;
+      if (rb.new_req) set_q<KFMT>(q, rb.qraw, a, cur.r, cur.seq, n);
+      // the block that takes this slot
+      Cur nxt = last;
+      const bool has_next = more && walk.next(nxt);
+      more = has_next;
+      const bool new_req = has_next && nxt.r != last.r;
+      __builtin_amdgcn_sched_barrier(0);
+      const bool full = kBlock * cur.b + (kBlock - 1) <= cur.seq - a.qlen;
+      const int lim = q.pos - kBlock * cur.b;
+      float m = -INFINITY;
+      compute_half<KFMT>(rb.h0, q, lut, tb, 0, full, lim, n, g, m);
+      __builtin_amdgcn_sched_barrier(0);
+      rb.qraw = issue_q<KFMT>(a, nxt.r, n, g, new_req);
+      issue_half<KFMT>(rb.h0, a, nxt.page, 0, n, g, has_next);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_half<KFMT>(rb.h1, q, lut, tb, 1, full, lim, n, g, m);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_half<KFMT>(rb.h1, a, nxt.page, 1, n, g, has_next);
+      __builtin_amdgcn_sched_barrier(0);
+      m = wave_max_xor(m, 16);
+      m = wave_max_xor(m, 32);
+      const bool writer = n < HQ && q.pos >= kBlock * cur.b;
+      const int64_t off = (int64_t)q.h * a.s_head + (int64_t)q.t * a.s_row + cur.b;
+      if constexpr (STAGED) {
+        if (g == 0 && n < HQ) {
+          stv[staged * HQ + n] = m * a.sm_scale;
+          sto[staged * HQ + n] = writer ? (int32_t)(off * 4) : 0x7FFFFFF0;
+        }
+        if (++staged == stage_blocks) {
+          flush_scores(srs, stv, sto, staged, HQ, lane);
+          staged = 0;
+        }
+      } else {
+        if (g == 0 && writer) a.scores[off] = m * a.sm_scale;
       }
-      if (++staged == stage_blocks) {
-        flush_scores(srs, stv, sto, staged, HQ, lane);
-        staged = 0;
-      }
-    } else {
-      if (g == 0 && writer) a.scores[off] = m * a.sm_scale;
+      rb.c = nxt;
+      rb.live = has_next;
+      rb.new_req = new_req;
+      if (has_next) last = nxt;
     }
-    if (!has_next) break;
-    if (new_req) set_q<KFMT>(q, qn, a, nxt.r, nxt.seq, n);
-    cur = nxt;
   }
+done:
   if constexpr (STAGED) flush_scores(srs, stv, sto, staged, HQ, lane);
 }
 
