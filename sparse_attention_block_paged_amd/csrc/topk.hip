@@ -10,8 +10,10 @@
 //
 // Design.  One wavefront per row.  Each lane holds the scores of blocks
 // lane, lane+64, ... as order-preserving u32 keys (forced blocks get the
-// largest key), so the k-th largest key T is found by a 32-step bitwise
-// search whose counts are wave ballots + scalar popcounts.  Blocks with
+// largest key), so the k-th largest key T is found by a bitwise search (at
+// most 32 steps) whose counts are wave ballots + scalar popcounts; it stops
+// as soon as exactly topk keys lie at or above the running threshold, since
+// no lower bit can change that set.  Blocks with
 // key > T are taken, and keys == T are taken in ascending id order until
 // topk are chosen; the same ballot prefix counts (mbcnt) give each chosen id
 // its output slot, so the row is written already sorted.  This replaces the
@@ -45,6 +47,7 @@ __device__ void select_regs(const float* srow, int nv, const TopkArgs& a, int32_
 #pragma unroll
     for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
     if (cnt >= a.topk) T = cand;
+    if (cnt == a.topk) break;  // exactly topk keys >= T: the rest of T cannot change the set
   }
   int gt = 0;
 #pragma unroll
@@ -71,6 +74,7 @@ __device__ void select_generic(const float* srow, int nv, const TopkArgs& a, int
     for (int b0 = 0; b0 < nv; b0 += 64)
       cnt += __popcll(__ballot(block_key(srow, b0 + lane, nv, a.init_blocks, a.local_blocks) >= cand));
     if (cnt >= a.topk) T = cand;
+    if (cnt == a.topk) break;
   }
   int gt = 0;
   for (int b0 = 0; b0 < nv; b0 += 64)
