@@ -182,6 +182,9 @@ EDGE = [
     ("prefill_many_tiles_mixed", dict(R=12, lens=(100, 5000), Q=700, H=4, max_seq_len=8192, topk=16,
                                       I=1, L=2)),
     ("prefill_h8_tail_tile", dict(R=3, lens=(1000, 3000), Q=65, H=8, max_seq_len=4096, topk=8, I=1, L=1)),
+    # selector with several rows per wave and a last wave short of rows
+    ("topk_rows_per_wave_ragged", dict(R=7, lens=(1400, 5000), Q=1301, H=1, max_seq_len=8192, topk=8,
+                                       I=1, L=1)),
     # tiles whose rows all sit before the first key (no steps) between live ones
     ("prefill_seq_shorter_than_q", dict(R=4, lens=(0, 0), Q=600, H=1, max_seq_len=1024, topk=4, I=1, L=1,
                                         fixed_lens=[100, 700, 0, 1])),
