@@ -120,7 +120,7 @@ def main():
     import torch
 
     import sparse_attention_block_paged_amd as mm3
-    from workloads import CONFIGS, config, host_subset
+    from workloads import WORKLOADS, config, host_subset
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -235,7 +235,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(base, seq, args.cpu_seconds)
 
-    cfg = CONFIGS[cid]
+    cfg = WORKLOADS[cid]
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),

@@ -112,8 +112,8 @@ typedef struct mm3_problem {
 
 /*
  * mm3_index_score -- block scores (page "ops.index_topk",
- * minimax_m3_index_score: "per-token index scores for each visible sparse
- * block", each "the max over a 128-token index-K block").
+ * minimax_m3_index_score): for every token row and head, one score per
+ * causally visible 128-token block, the block's largest scaled dot product.
  *   scores  fp32, element (h, t, b) at scores[h*s_head_stride + t*s_row_stride + b],
  *           s_width >= cdiv(max_seq_len,128) columns per row,
  *           s_row_stride >= s_width, s_head_stride >= tokens*s_row_stride.
@@ -122,7 +122,8 @@ typedef struct mm3_problem {
  *           dot product of q[t, h, :] and the key).
  * Rows with H*query_len <= 16 per request use the bandwidth-bound decode
  * scorer; larger ones the MFMA prefill scorer.  NVFP4 keys: decode shapes only
- * (MM3_EUNSUPPORTED otherwise).
+ * (MM3_EUNSUPPORTED otherwise).  q and keys are expected finite: a score
+ * whose block holds a NaN or infinite product is unspecified.
  */
 int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
                     int64_t s_row_stride, int32_t s_width, void* stream);

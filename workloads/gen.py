@@ -90,8 +90,8 @@ def round_up(a: int, b: int) -> int:
 
 
 # The five workloads: (name, R, len range, Q, H, max_seq_len, topk, I, L,
-# key format, extras).  Seeds are the config numbers.
-CONFIGS = {
+# key format, extras).  Each workload is seeded with its number.
+WORKLOADS = {
     1: dict(name="tiny_decode", R=1, lens=(1000, 1000), Q=4, H=1,
             max_seq_len=2048, topk=4, I=1, L=1, kfmt=KFMT_BF16, pool=16),
     2: dict(name="decode_batch", R=64, lens=(4096, 32768), Q=4, H=4,
@@ -108,7 +108,7 @@ CONFIGS = {
 
 
 def config(cid: int, device="cpu", seed: Optional[int] = None, **override) -> Workload:
-    c = dict(CONFIGS[cid])
+    c = dict(WORKLOADS[cid])
     c.update(override)
     return make(seed=cid if seed is None else seed, device=device, **c)
 
