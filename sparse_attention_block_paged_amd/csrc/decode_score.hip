@@ -483,12 +483,14 @@ struct BalancedWalk {
   const int32_t* pre;  // LDS: pre[r] = blocks of requests < r
   const int32_t* sl;   // LDS: seq_lens
   int64_t gb, hi;      // this wave's next flattened block, slice end
+  int64_t req_hi;      // first flattened block past the current request
 
   __device__ __forceinline__ int count() const { return (int)(hi - gb); }  // valid after first()
 
   __device__ __forceinline__ void fill(Cur& c) {
     c.b = __builtin_amdgcn_readfirstlane((int)(gb - pre[c.r]));
     c.seq = __builtin_amdgcn_readfirstlane(sl[c.r]);
+    req_hi = __builtin_amdgcn_readfirstlane(pre[c.r + 1]);
     // finish the LDS reads before the scalar page load, so that later waits
     // on LDS never also wait on that load
     __builtin_amdgcn_sched_barrier(0);
@@ -508,6 +510,11 @@ struct BalancedWalk {
   __device__ __forceinline__ bool next(Cur& c) {
     ++gb;
     if (gb >= hi) return false;
+    if (gb < req_hi) {  // same request: next block, no LDS lookups
+      ++c.b;
+      c.page = page_of(*a, c.r, c.b);
+      return true;
+    }
     int r = c.r;
     while (pre[r + 1] <= gb) ++r;
     c.r = __builtin_amdgcn_readfirstlane(r);
@@ -559,7 +566,7 @@ __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
   // each wave takes a contiguous quarter of the slice, so consecutive blocks
   // of a row (and their score writes) stay with one wave
   const int64_t span = hi - lo;
-  BalancedWalk walk{&a, pre, sl, lo + span * wave / 4, lo + span * (wave + 1) / 4};
+  BalancedWalk walk{&a, pre, sl, lo + span * wave / 4, lo + span * (wave + 1) / 4, 0};
   score_wave<KFMT, true>(a, lut, tbuf[wave], walk, stage_v[wave], stage_o[wave]);
 }
 
