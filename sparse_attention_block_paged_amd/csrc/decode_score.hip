@@ -527,7 +527,7 @@ template <int KFMT>
 __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
   extern __shared__ int32_t smem[];
   __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
-  __shared__ int32_t part[256];
+  __shared__ int32_t part[4];
   __shared__ float stage_v[4][kStage];
   __shared__ int32_t stage_o[4][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[4][KFMT == 0 ? kTransposeBytes : 16];
@@ -542,22 +542,31 @@ __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
     sl[r] = s;
     sum += s > 0 ? (s - 1) / kBlock + 1 : 0;
   }
-  part[threadIdx.x] = sum;
   if constexpr (KFMT == 1) fill_lut(lut);
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the partial sums
-    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
+  // exclusive scan of the 256 partial sums: within each wave by lane shifts,
+  // then over the four wave totals (two barriers in all)
+  const int lane = threadIdx.x & 63;
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
   }
-  int base = threadIdx.x ? part[threadIdx.x - 1] : 0;
+  if (lane == 63) part[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  int base = incl - sum, total_blocks = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int pw = part[w];
+    base += w < (int)(threadIdx.x >> 6) ? pw : 0;
+    total_blocks += pw;
+  }
   for (int r = r0; r < r1; ++r) {
     pre[r] = base;
     const int s = sl[r];
     base += s > 0 ? (s - 1) / kBlock + 1 : 0;
   }
-  if (threadIdx.x == 255) pre[R] = part[255];
+  if (threadIdx.x == 255) pre[R] = total_blocks;
   __syncthreads();
   const int64_t total = pre[R];
   const int64_t lo = total * blockIdx.x / gridDim.x;
