@@ -470,48 +470,60 @@ __device__ __forceinline__ void fill_lut(u32x2* lut) {
   lut[threadIdx.x].y = kFp4Lut.w[threadIdx.x][1];
 }
 
-// ---- length-balanced persistent scorer
+// ---- per-CU scorer
 //
-// A fixed grid (a few workgroups per CU) shares all (request, block) pairs of
-// the batch equally: each workgroup builds the prefix sum of the requests'
-// block counts in LDS, takes one contiguous slice of the flattened block
-// list, and each of its four waves takes a contiguous quarter of it.  Every wave
-// streams pages continuously; no workgroup idles on a short request.
+// One workgroup per CU holds all of the CU's waves.  The batch's (request,
+// block) pairs, flattened request-major, are cut into equal contiguous slices,
+// one per workgroup (each builds the prefix sum of the requests' block counts
+// in LDS to map a flattened index back to its request).  Inside a workgroup
+// the waves take the slice's blocks one at a time from an LDS counter, so a
+// wave the SIMD arbiter favours simply scores more blocks: with fixed
+// per-wave shares the waves of one CU finished up to ~50% apart and the CU
+// idled on its slowest wave.  The slices of all CUs finish within a few
+// percent of each other.
 
-struct BalancedWalk {
+struct SharedWalk {
   const ScoreArgs* a;
   const int32_t* pre;  // LDS: pre[r] = blocks of requests < r
   const int32_t* sl;   // LDS: seq_lens
-  int64_t gb, hi;      // this wave's next flattened block, slice end
-  int64_t req_hi;      // first flattened block past the current request
+  uint32_t* counter;   // LDS: next block of the slice, counted from lo
+  int64_t lo, hi;      // the workgroup's slice of the flattened block list
+  int64_t gb;          // the block just taken
+  int64_t req_lo, req_hi;  // flattened range of the current request
 
-  __device__ __forceinline__ int count() const { return (int)(hi - gb); }  // valid after first()
-
+  __device__ __forceinline__ bool take() {
+    uint32_t v = 0;
+    if ((threadIdx.x & 63) == 0) v = atomicAdd(counter, 1u);
+    gb = lo + (int64_t)__builtin_amdgcn_readfirstlane(v);
+    return gb < hi;
+  }
   __device__ __forceinline__ void fill(Cur& c) {
-    c.b = __builtin_amdgcn_readfirstlane((int)(gb - pre[c.r]));
-    c.seq = __builtin_amdgcn_readfirstlane(sl[c.r]);
+    req_lo = __builtin_amdgcn_readfirstlane(pre[c.r]);
     req_hi = __builtin_amdgcn_readfirstlane(pre[c.r + 1]);
+    c.seq = __builtin_amdgcn_readfirstlane(sl[c.r]);
+    c.b = (int)(gb - req_lo);
     // finish the LDS reads before the scalar page load, so that later waits
     // on LDS never also wait on that load
     __builtin_amdgcn_sched_barrier(0);
     c.page = page_of(*a, c.r, c.b);
   }
   __device__ __forceinline__ bool first(Cur& c) {
-    if (gb >= hi) return false;
-    int lo = 0, up = a->num_reqs;  // last r with pre[r] <= gb
-    while (up - lo > 1) {
-      const int mid = (lo + up) >> 1;
-      if (pre[mid] <= gb) lo = mid; else up = mid;
+    if (!take()) return false;
+    int l = 0, u = a->num_reqs;  // last r with pre[r] <= gb
+    while (u - l > 1) {
+      const int mid = (l + u) >> 1;
+      if (pre[mid] <= gb) l = mid; else u = mid;
     }
-    c.r = __builtin_amdgcn_readfirstlane(lo);
+    c.r = __builtin_amdgcn_readfirstlane(l);
     fill(c);
     return true;
   }
+  // blocks come out of the counter in increasing order, so the request only
+  // moves forward
   __device__ __forceinline__ bool next(Cur& c) {
-    ++gb;
-    if (gb >= hi) return false;
-    if (gb < req_hi) {  // same request: next block, no LDS lookups
-      ++c.b;
+    if (!take()) return false;
+    if (gb < req_hi) {
+      c.b = (int)(gb - req_lo);
       c.page = page_of(*a, c.r, c.b);
       return true;
     }
@@ -523,18 +535,25 @@ struct BalancedWalk {
   }
 };
 
+// waves per workgroup (= per CU): what the register budget allows
 template <int KFMT>
-__global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
+constexpr int kCuWaves = KFMT == 0 ? 8 : 16;
+
+template <int KFMT>
+__global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs a) {
+  constexpr int W = kCuWaves<KFMT>;
+  constexpr int NT = 64 * W;
   extern __shared__ int32_t smem[];
   __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
-  __shared__ int32_t part[4];
-  __shared__ float stage_v[4][kStage];
-  __shared__ int32_t stage_o[4][kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t tbuf[4][KFMT == 0 ? kTransposeBytes : 16];
+  __shared__ int32_t part[W];
+  __shared__ uint32_t next_blk;
+  __shared__ float stage_v[W][kStage];
+  __shared__ int32_t stage_o[W][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[W][KFMT == 0 ? kTransposeBytes : 16];
   const int R = a.num_reqs;
-  int32_t* pre = smem;        // [R + 1]
+  int32_t* pre = smem;         // [R + 1]
   int32_t* sl = smem + R + 1;  // [R]
-  const int per = (R + 255) / 256;
+  const int per = (R + NT - 1) / NT;
   const int r0 = min(R, (int)threadIdx.x * per), r1 = min(R, r0 + per);
   int sum = 0;
   for (int r = r0; r < r1; ++r) {
@@ -542,23 +561,27 @@ __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
     sl[r] = s;
     sum += s > 0 ? (s - 1) / kBlock + 1 : 0;
   }
-  if constexpr (KFMT == 1) fill_lut(lut);
-  // exclusive scan of the 256 partial sums: within each wave by lane shifts,
-  // then over the four wave totals (two barriers in all)
+  if constexpr (KFMT == 1) {
+    if (threadIdx.x < 256) fill_lut(lut);
+  }
+  // exclusive scan of the partial sums: within each wave by lane shifts,
+  // then over the wave totals (two barriers in all)
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   int incl = sum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int o = __shfl_up(incl, d);
     if (lane >= d) incl += o;
   }
-  if (lane == 63) part[threadIdx.x >> 6] = incl;
+  if (lane == 63) part[wave] = incl;
+  if (threadIdx.x == 0) next_blk = 0;
   __syncthreads();
   int base = incl - sum, total_blocks = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < W; ++w) {
     const int pw = part[w];
-    base += w < (int)(threadIdx.x >> 6) ? pw : 0;
+    base += w < wave ? pw : 0;
     total_blocks += pw;
   }
   for (int r = r0; r < r1; ++r) {
@@ -566,16 +589,12 @@ __global__ __launch_bounds__(256) void decode_score_balanced(ScoreArgs a) {
     const int s = sl[r];
     base += s > 0 ? (s - 1) / kBlock + 1 : 0;
   }
-  if (threadIdx.x == 255) pre[R] = total_blocks;
+  if (threadIdx.x == NT - 1) pre[R] = total_blocks;
   __syncthreads();
-  const int64_t total = pre[R];
+  const int64_t total = total_blocks;
   const int64_t lo = total * blockIdx.x / gridDim.x;
   const int64_t hi = total * (blockIdx.x + 1) / gridDim.x;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // each wave takes a contiguous quarter of the slice, so consecutive blocks
-  // of a row (and their score writes) stay with one wave
-  const int64_t span = hi - lo;
-  BalancedWalk walk{&a, pre, sl, lo + span * wave / 4, lo + span * (wave + 1) / 4, 0};
+  SharedWalk walk{&a, pre, sl, &next_blk, lo, hi, 0, 0, 0};
   score_wave<KFMT, true>(a, lut, tbuf[wave], walk, stage_v[wave], stage_o[wave]);
 }
 
@@ -626,8 +645,8 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
 
 // ------------------------------------------------------------------ launch
 
-// Largest batch whose lengths and prefix sums fit the balanced scorer's LDS.
-constexpr int kBalancedMaxReqs = 8192;
+// Largest batch whose lengths and prefix sums fit the per-CU scorer's LDS.
+constexpr int kCuMaxReqs = 4096;
 
 int device_cus() {
   static int cache[64] = {0};
@@ -641,28 +660,12 @@ int device_cus() {
   return cache[dev];
 }
 
-// Workgroups of the balanced scorer resident per CU with `lds` bytes of
-// dynamic LDS (cached per 1 KiB step of LDS).
-template <int KFMT>
-static int balanced_occupancy(size_t lds) {
-  static int cache[(2 * kBalancedMaxReqs + 1) * 4 / 1024 + 2] = {0};
-  const size_t key = (lds + 1023) / 1024;
-  if (!cache[key]) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_score_balanced<KFMT>, 256, key * 1024) !=
-            hipSuccess || v <= 0)
-      v = 1;
-    cache[key] = v;
-  }
-  return cache[key];
-}
-
 template <int KFMT>
 static hipError_t launch_decode(const ScoreArgs& a, hipStream_t s) {
   const size_t lds = (size_t)(2 * a.num_reqs + 1) * sizeof(int32_t);
-  if (a.num_reqs <= kBalancedMaxReqs && a.s_bytes > 0) {
-    const int grid = device_cus() * balanced_occupancy<KFMT>(lds);
-    hipLaunchKernelGGL(decode_score_balanced<KFMT>, dim3(grid), dim3(256), lds, s, a);
+  if (a.num_reqs <= kCuMaxReqs && a.s_bytes > 0) {
+    // one workgroup per CU: its LDS and registers leave room for no second
+    hipLaunchKernelGGL(decode_score_cu<KFMT>, dim3(device_cus()), dim3(64 * kCuWaves<KFMT>), lds, s, a);
   } else {
     const int chunks = (a.nb_max + a.blocks_per_wg - 1) / a.blocks_per_wg;
     hipLaunchKernelGGL(decode_score_chunked<KFMT>, dim3(chunks, a.num_reqs, 1), dim3(256), 0, s, a);
