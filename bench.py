@@ -226,8 +226,8 @@ def main():
         achieved = alg["scorer_bytes"] / (ms_score * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=recorded_traffic(base.name, "decode_score_balanced<%d>" % base.kfmt),
-                    kernel="decode_score_balanced<%d>" % base.kfmt, ms=round(ms_score, 4),
+                    traffic=recorded_traffic(base.name, "decode_score_cu<%d>" % base.kfmt),
+                    kernel="decode_score_cu<%d>" % base.kfmt, ms=round(ms_score, 4),
                     per_launch_bytes=alg["scorer_bytes"])
     sel_gbs = alg["selector_bytes"] / (ms_topk * 1e-3) / 1e9
 
@@ -324,7 +324,7 @@ def summarize_rocprof(d, label, record):
             rec = json.load(open(path)) if os.path.exists(path) else {}
             for (kern, cname), vals in per.items():
                 short = kern.split("(")[0].replace("void ", "").replace("mm3::", "")
-                if not short.startswith(("decode_score_balanced", "prefill_score_kernel")):
+                if not short.startswith(("decode_score_cu", "prefill_score_kernel")):
                     continue
                 if cname not in calib:
                     continue
