@@ -52,7 +52,7 @@ extern "C" {
 /* return codes */
 #define MM3_OK 0
 #define MM3_EINVAL (-1)       /* an argument breaks a rule listed below */
-#define MM3_EUNSUPPORTED (-2) /* valid, but not implemented by this build */
+#define MM3_EUNSUPPORTED (-2) /* valid, but not implemented (reserved; no call returns it now) */
 #define MM3_EWORKSPACE (-3)   /* workspace NULL, misaligned or too small */
 #define MM3_EHIP (-4)         /* a HIP launch failed; message has the HIP error */
 
@@ -121,9 +121,10 @@ typedef struct mm3_problem {
  *   score = fl32(sm_scale * max over visible tokens of the fp32-accumulated
  *           dot product of q[t, h, :] and the key).
  * Rows with H*query_len <= 16 per request use the bandwidth-bound decode
- * scorer; larger ones the MFMA prefill scorer.  NVFP4 keys: decode shapes only
- * (MM3_EUNSUPPORTED otherwise).  q and keys are expected finite: a score
- * whose block holds a NaN or infinite product is unspecified.
+ * scorer; larger ones the MFMA prefill scorer.  Both take either key format
+ * (the prefill scorer decodes each NVFP4 page once into bf16 in LDS).  q and
+ * keys are expected finite: a score whose block holds a NaN or infinite
+ * product is unspecified.
  */
 int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
                     int64_t s_row_stride, int32_t s_width, void* stream);

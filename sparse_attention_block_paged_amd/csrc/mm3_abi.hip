@@ -147,14 +147,8 @@ int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStr
   if (is_decode_shape(p))
     e = p->kfmt == MM3_KFMT_BF16 ? launch_decode_score_bf16(a, st) : launch_decode_score_nvfp4(a, st);
   else
-    e = launch_prefill_score_bf16(a, st);
+    e = p->kfmt == MM3_KFMT_BF16 ? launch_prefill_score_bf16(a, st) : launch_prefill_score_nvfp4(a, st);
   return e == hipSuccess ? MM3_OK : hip_fail(e, "scorer launch");
-}
-
-int check_shape_supported(const mm3_problem* p) {
-  if (!is_decode_shape(p) && p->kfmt != MM3_KFMT_BF16)
-    return fail(MM3_EUNSUPPORTED, "NVFP4 keys are scored for heads*query_len <= 16 only");
-  return MM3_OK;
 }
 
 TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t heads, const int32_t* seq,
@@ -193,7 +187,6 @@ int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_scores(p, scores, s_head_stride, s_row_stride, s_width))) return rc;
-  if ((rc = check_shape_supported(p))) return rc;
   if ((int64_t)p->num_reqs * p->query_len == 0 || p->max_seq_len == 0) return ok();
   if ((rc = launch_scores(p, scores, s_head_stride, s_row_stride, (hipStream_t)stream))) return rc;
   return ok();
@@ -249,7 +242,6 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
   const int64_t T = (int64_t)p->num_reqs * p->query_len;
   if ((rc = check_out(out, o_head_stride, o_row_stride, p->heads, T, topk))) return rc;
-  if ((rc = check_shape_supported(p))) return rc;
   float* s = scores_out;
   int64_t sh = s_head_stride, sr = s_row_stride;
   int32_t sw = s_width;

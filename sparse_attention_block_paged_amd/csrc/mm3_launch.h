@@ -67,6 +67,7 @@ struct SparseTableArgs {
 hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_prefill_score_nvfp4(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s);
 

@@ -33,6 +33,7 @@
 // Two workgroups (80 KiB of LDS each) share a CU, so one's barrier or copy
 // wait is covered by the other's multiplies.
 #include "mm3_device.h"
+#include "mm3_fp4.h"
 #include "mm3_launch.h"
 
 namespace mm3 {
@@ -50,6 +51,18 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfCopies = kPageBytes / (kPfThreads * 16);    // 16-byte copies per thread per page
 constexpr int kPfStageFloats = kPfWaveRows * kPfStage;       // per wave
 constexpr int kPfLds = 2 * kPageBytes + kPfWaves * kPfStageFloats * 4;  // 80 KiB
+// NVFP4 keys: the page (8 KiB nibbles + 1 KiB scales) is copied into one of
+// two staging slots, then decoded once by the whole workgroup into a single
+// bf16 page buffer in the same swizzled layout.
+constexpr int kFp4NibBytes = kBlock * kDim / 2;    // 8 KiB
+constexpr int kFp4ScaleBytes = kBlock * kDim / 16;  // 1 KiB
+constexpr int kPfFp4Stage0 = kPageBytes;                             // nibble slots
+constexpr int kPfFp4Scale0 = kPfFp4Stage0 + 2 * kFp4NibBytes;       // scale slots
+constexpr int kPfFp4Lut = kPfFp4Scale0 + 2 * kFp4ScaleBytes;        // E4M3 table
+constexpr int kPfFp4Scores = kPfFp4Lut + 256 * 8;                   // score stage
+constexpr int kPfLdsFp4 = kPfFp4Scores + kPfWaves * kPfStageFloats * 4;  // 68 KiB
+template <int KFMT>
+constexpr int kPfLdsOf = KFMT == 0 ? kPfLds : kPfLdsFp4;
 // Above this many (request, row tile) units the start-finding scan of the
 // balanced grid costs more than it saves: one workgroup per unit instead.
 constexpr int kPfBalancedMaxUnits = 1 << 16;
@@ -98,17 +111,29 @@ __device__ __forceinline__ void ring_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier after LDS writes only: copies still in flight are not
+// waited for.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Position in the list of (unit, block) steps.
 struct PfCursor {
   int u, r, x, seq, nv, b;
 };
 
-template <bool BALANCED>
+template <int KFMT, bool BALANCED>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs a, int units, int tiles) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLdsOf<KFMT>];
+  // bf16: two page buffers.  NVFP4: one decoded page buffer plus two staging
+  // slots for the raw page.
   uint8_t* const kbuf0 = smem;
   uint8_t* const kbuf1 = smem + kPageBytes;
-  float* const stage_all = reinterpret_cast<float*>(smem + 2 * kPageBytes);
+  float* const stage_all = reinterpret_cast<float*>(smem + (KFMT == 0 ? 2 * kPageBytes : kPfFp4Scores));
+  u32x2* const lut = reinterpret_cast<u32x2*>(smem + kPfFp4Lut);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads, Q = a.qlen, HQ = H * Q;
@@ -208,7 +233,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
       pos_q[qt] = ok ? cur.seq - Q + j : -1;
       const uint16_t* qp = a.q + (int64_t)(cur.r * Q + j) * a.q_tok + (int64_t)h * a.q_head;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qb[qt][kk] = as_bf16x8(ld16(qp + 16 * kk + 8 * kg));
+      for (int kk = 0; kk < 8; ++kk) {
+        const u32x4 v = ld16(qp + 16 * kk + 8 * kg);
+        if constexpr (KFMT == 0) {
+          qb[qt][kk] = as_bf16x8(v);
+        } else {
+          // decoded NVFP4 chunks hold their 8 elements in the order
+          // {0,2,4,6,1,3,5,7}; the query operand follows it
+          u32x4 pv;
+          pv.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+          pv.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+          pv.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+          pv.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
+          qb[qt][kk] = as_bf16x8(pv);
+        }
+      }
     }
     wave_live = wrow0 < HQ;
     wave_pos_min = cur.seq - Q + min(wrow0, HQ - 1) / H;
@@ -229,6 +268,36 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     // the 4 KiB steps go on the scalar base: one offset register for all
 #pragma unroll
     for (int k = 0; k < kPfCopies; ++k) copy16_to_lds(l0 + 4096 * k, pg + 4096 * k, src0);
+  };
+
+  // NVFP4: copy k (0, 1) of wave w moves nibble KiB 4k + w of the page, and
+  // wave 0 also moves the 1 KiB of scales, into staging slot `slot`.
+  auto copy_fp4 = [&](int slot, const PfCursor& c) __attribute__((always_inline)) {
+    const int64_t page = bt_s[(int64_t)c.r * a.bt_stride + c.b];
+    const uint8_t* nib = a.kdata + page * kFp4NibBytes;
+    const uint32_t l0 =
+        (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Stage0 + slot * kFp4NibBytes) + 1024 * wave;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) copy16_to_lds(l0 + 4096 * k, nib + 4096 * k + 1024 * wave, 16 * lane);
+    if (wave == 0)
+      copy16_to_lds((uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Scale0 + slot * kFp4ScaleBytes),
+                    a.kscales + page * kFp4ScaleBytes, 16 * lane);
+  };
+  // decode staging slot `slot` into kbuf0: thread t handles the 16-byte
+  // chunks t + 256j (token q/16, chunk q%16 = dims 8(q%16)..+8)
+  auto decode_fp4 = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* nib = smem + kPfFp4Stage0 + slot * kFp4NibBytes;
+    const uint8_t* scl = smem + kPfFp4Scale0 + slot * kFp4ScaleBytes;
+    // two chunks at a time: all eight in flight would need registers that
+    // the query operands and accumulators hold
+#pragma unroll 2
+    for (int j = 0; j < kBlock * 16 / kPfThreads; ++j) {
+      const int qc = threadIdx.x + kPfThreads * j;
+      const int tok = qc >> 4, c = qc & 15;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(nib + tok * (kDim / 2) + 4 * c);
+      const u32x2 tab = lut[scl[tok * (kDim / 16) + (c >> 1)]];
+      *reinterpret_cast<u32x4*>(kbuf0 + swz(tok, c)) = fp4x8_to_bf16(x, tab);
+    }
   };
 
   float* const stage = stage_all + wave * kPfStageFloats;
@@ -326,16 +395,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
 
   // ---- the ring: block of step i sits in buffer i & 1; the copy of step
   // i + 1 is started once every wave is past step i - 1.
+  if constexpr (KFMT == 1) fill_lut(lut);  // read after the first ring barrier
   load_q();
   PfCursor nxt = cur;
-  copy_page(kbuf0, nxt);
+  if constexpr (KFMT == 0)
+    copy_page(kbuf0, nxt);
+  else
+    copy_fp4(0, nxt);
   int bfirst = cur.b, nst = 0;
   for (int i = 0; i < nsteps; ++i) {
-    uint8_t* const kl = (i & 1) ? kbuf1 : kbuf0;
+    uint8_t* const kl = (KFMT == 0 && (i & 1)) ? kbuf1 : kbuf0;
     ring_sync();
     if (i + 1 < nsteps) {
       advance(nxt);
-      copy_page((i & 1) ? kbuf0 : kbuf1, nxt);
+      if constexpr (KFMT == 0)
+        copy_page((i & 1) ? kbuf0 : kbuf1, nxt);
+      else
+        copy_fp4((i + 1) & 1, nxt);
+    }
+    if constexpr (KFMT == 1) {
+      // every wave is past step i - 1 (the ring barrier), so kbuf0 is free
+      decode_fp4(i & 1);
+      lds_sync();
     }
     compute(kl, cur.b, nst);
     ++nst;
@@ -356,13 +437,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
   }
 }
 
+template <int KFMT>
 static int prefill_grid() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!cache[dev]) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_score_kernel<true>, kPfThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_score_kernel<KFMT, true>, kPfThreads, 0) !=
             hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
@@ -371,18 +453,23 @@ static int prefill_grid() {
   return cache[dev];
 }
 
-hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s) {
+template <int KFMT>
+static hipError_t launch_prefill(const ScoreArgs& a, hipStream_t s) {
   const int tiles = (a.heads * a.qlen + kPrefillRows - 1) / kPrefillRows;
   const int64_t units = (int64_t)a.num_reqs * tiles;
   // the scan counts steps in 32-bit integers
   if (units <= kPfBalancedMaxUnits && units * a.nb_max <= INT32_MAX) {
-    hipLaunchKernelGGL(prefill_score_kernel<true>, dim3(prefill_grid()), dim3(kPfThreads), 0, s, a, (int)units,
-                       tiles);
+    hipLaunchKernelGGL((prefill_score_kernel<KFMT, true>), dim3(prefill_grid<KFMT>()), dim3(kPfThreads), 0, s, a,
+                       (int)units, tiles);
   } else {
-    hipLaunchKernelGGL(prefill_score_kernel<false>, dim3((unsigned)units), dim3(kPfThreads), 0, s, a, (int)units,
-                       tiles);
+    hipLaunchKernelGGL((prefill_score_kernel<KFMT, false>), dim3((unsigned)units), dim3(kPfThreads), 0, s, a,
+                       (int)units, tiles);
   }
   return hipGetLastError();
 }
+
+hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s) { return launch_prefill<0>(a, s); }
+
+hipError_t launch_prefill_score_nvfp4(const ScoreArgs& a, hipStream_t s) { return launch_prefill<1>(a, s); }
 
 }  // namespace mm3

@@ -125,12 +125,6 @@ def test_score_buffer_rules(label, kw, msg):
     assert msg in _err(), _err()
 
 
-def test_nvfp4_prefill_shape_unsupported():
-    p = _problem(kfmt=1, kscales=FAKE * 8, query_len=64)
-    assert _score(p) == B.MM3_EUNSUPPORTED
-    assert "NVFP4" in _err()
-
-
 def test_empty_batch_returns_ok_without_launch():
     assert _score(_problem(num_reqs=0)) == B.MM3_OK
     assert _err() == ""

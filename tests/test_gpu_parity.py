@@ -70,6 +70,8 @@ SMALL = {
     "long_decode_small": dict(cid=3, R=6, lens=(3000, 16000), max_seq_len=16384),
     "prefill_small": dict(cid=4, R=2, lens=(700, 1500), Q=333, max_seq_len=2048),
     "nvfp4_small": dict(cid=5, R=8, lens=(1000, 9000), max_seq_len=9216),
+    # NVFP4 keys under the prefill scorer (pages decoded into LDS)
+    "prefill_nvfp4_small": dict(cid=4, R=2, lens=(700, 1500), Q=333, max_seq_len=2048, kfmt=KFMT_NVFP4),
 }
 
 
@@ -86,7 +88,7 @@ def test_small_split(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_decode", "decode_batch_small", "long_decode_small",
-                                  "nvfp4_small", "prefill_small"])
+                                  "nvfp4_small", "prefill_small", "prefill_nvfp4_small"])
 def test_small_fused(name):
     kw = dict(SMALL[name])
     cid = kw.pop("cid")
@@ -203,6 +205,44 @@ def test_edge_cases(label, kw):
     if w.heads * w.query_len <= 16:
         _, out2 = run_fused(w, with_scores=False)
         assert torch.equal(out, out2)
+
+
+NVFP4_PREFILL_EDGE = [
+    ("nvfp4_prefill_h1_ragged", dict(R=3, lens=(300, 2600), Q=300, H=1, max_seq_len=4096, topk=8, I=1, L=1)),
+    ("nvfp4_prefill_tail_tile", dict(R=2, lens=(900, 3000), Q=65, H=8, max_seq_len=4096, topk=8, I=1, L=2)),
+    ("nvfp4_prefill_seq_shorter_than_q", dict(R=3, lens=(0, 0), Q=600, H=1, max_seq_len=1024, topk=4, I=1,
+                                              L=1, fixed_lens=[100, 700, 1])),
+]
+
+
+@pytest.mark.parametrize("label,kw", NVFP4_PREFILL_EDGE, ids=[e[0] for e in NVFP4_PREFILL_EDGE])
+def test_nvfp4_prefill_edges(label, kw):
+    w = make(name=label, kfmt=KFMT_NVFP4, seed=len(label) + 3, device=DEV, **kw)
+    _say(f"edge {label}")
+    scores, out = run_split(w)
+    full_check(w, scores, out, label)
+    P.check_invariants(out.cpu().numpy(), w.seq_lens.cpu().numpy(), w.query_len, w.topk,
+                       w.init_blocks, w.local_blocks)
+
+
+def test_full_size_prefill_nvfp4():
+    """The chunked-prefill shape with NVFP4 keys: sampled rows of two
+    requests against the oracle, selection invariants on every row."""
+    w = config(4, device=DEV, kfmt=KFMT_NVFP4)
+    _say(f"full NVFP4 prefill: R={w.num_reqs} Q={w.query_len} H={w.heads}")
+    scores, out = run_split(w)
+    P.check_invariants(out.cpu().numpy(), w.seq_lens.cpu().numpy(), w.query_len, w.topk,
+                       w.init_blocks, w.local_blocks)
+    rng = np.random.default_rng(9)
+    for r in [1, 2]:
+        a, rows = host_subset(w, [r])
+        loc = sorted(set([0, 127, 128, 8191] + rng.integers(0, 8192, 6).tolist()))
+        s_ref, ids_ref = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks,
+                                          rows=loc)
+        err = P.check_scores(scores[:, rows].cpu().numpy(), s_ref, rows=loc)
+        near = P.check_ids(out[:, rows].cpu().numpy(), ids_ref, s_ref, a["seq_lens"], w.query_len,
+                           w.topk, w.init_blocks, w.local_blocks, rows=loc)
+        _say(f"full NVFP4 prefill req {r}: {len(loc)} sampled rows, max err {err:.3g}, near-tie rows {near}")
 
 
 def test_nvfp4_edge_short():

@@ -104,6 +104,9 @@ WORKLOADS = {
             max_seq_len=16384, topk=16, I=1, L=2, kfmt=KFMT_BF16),
     5: dict(name="nvfp4_decode", R=128, lens=(16384, 65536), Q=4, H=1,
             max_seq_len=65536, topk=16, I=1, L=2, kfmt=KFMT_NVFP4),
+    # beyond the five: the chunked-prefill shape with NVFP4 keys
+    6: dict(name="chunked_prefill_nvfp4", R=4, lens=(16384, 16384), Q=8192, H=4,
+            max_seq_len=16384, topk=16, I=1, L=2, kfmt=KFMT_NVFP4),
 }
 
 
