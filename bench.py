@@ -219,8 +219,8 @@ def main():
         achieved = alg["flops"] / (ms_score * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                    traffic=recorded_traffic(base.name, "prefill_score_kernel<true>"),
-                    kernel="prefill_score_kernel<true>", ms=round(ms_score, 4),
+                    traffic=recorded_traffic(base.name, "prefill_score_kernel<%d, true>" % base.kfmt),
+                    kernel="prefill_score_kernel<%d, true>" % base.kfmt, ms=round(ms_score, 4),
                     per_launch_flops=alg["flops"])
     else:
         achieved = alg["scorer_bytes"] / (ms_score * 1e-3) / 1e9
