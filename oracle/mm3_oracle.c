@@ -24,6 +24,12 @@
  * Readings taken where the pages are silent (each is listed with its reason
  * in the repository's design notes):
  *   - the Q rows of request r sit at positions seq_len[r]-Q+j, j<Q;
+ *   - ragged batches (minimax_m3_index_score / minimax_m3_index_topk take
+ *     cu_seqlens_q and prefix_lens): request r owns rows
+ *     [cu_seqlens_q[r], cu_seqlens_q[r+1]) and its row j sits at position
+ *     prefix_lens[r] + j; without prefix_lens (the NVFP4 prefill scorer of
+ *     page "indexer_nvfp4" takes only cu_seqlens_q and seq_lens) the rows are
+ *     the request's last tokens, seq_lens[r] - n_r + j;
  *   - a row at position pos sees blocks b <= pos/128, and in block b the
  *     tokens 128b+s <= pos;
  *   - forced blocks take slots inside topk; init and local overlap is
@@ -110,6 +116,46 @@ double oracle_nvfp4_element(int nib, int scale_byte)
                                     oracle_e4m3_value(scale_byte));
 }
 
+/* ---------------------------------------------------------- row mapping */
+
+/*
+ * Request and position of row t.  Uniform batches (cu == NULL): request
+ * r = t / Q owns rows [rQ, rQ+Q) and its row j sits at seq_lens[r] - Q + j.
+ * Ragged batches: r is the request with cu[r] <= t < cu[r+1] (found by a
+ * plain scan), j = t - cu[r], and the position is prefix[r] + j, or
+ * seq_lens[r] - (cu[r+1] - cu[r]) + j without prefix.  Returns 0, or -1 when
+ * t is outside the batch.
+ */
+static int orc_row(int64_t t, const int32_t* seq_lens, int num_reqs,
+                   int query_len, const int32_t* cu, const int32_t* prefix,
+                   int* r_out, int64_t* pos_out)
+{
+    if (!cu) {
+        if (t < 0 || t >= (int64_t)num_reqs * query_len)
+            return -1;
+        int r = (int)(t / query_len);
+        *r_out = r;
+        *pos_out = (int64_t)seq_lens[r] - query_len + (t % query_len);
+        return 0;
+    }
+    for (int r = 0; r < num_reqs; ++r) {
+        if (cu[r] <= t && t < cu[r + 1]) {
+            int64_t j = t - cu[r];
+            int64_t n = (int64_t)cu[r + 1] - cu[r];
+            *r_out = r;
+            *pos_out = prefix ? (int64_t)prefix[r] + j
+                              : (int64_t)seq_lens[r] - n + j;
+            return 0;
+        }
+    }
+    return -1;
+}
+
+static int64_t orc_total_rows(int num_reqs, int query_len, const int32_t* cu)
+{
+    return cu ? (int64_t)cu[num_reqs] : (int64_t)num_reqs * query_len;
+}
+
 /* ------------------------------------------------------------ block scores */
 
 typedef struct {
@@ -143,7 +189,7 @@ static double orc_key(int kfmt, const void* kdata, const uint8_t* kscales,
 
 /*
  * Block scores.  For every requested row t (all rows when rows == NULL):
- *   r = t / Q, j = t % Q, pos = seq_lens[r] - Q + j; rows with pos < 0 see
+ *   request r and position pos as orc_row gives them; rows with pos < 0 see
  *   nothing and are skipped.  For head h and visible block b <= pos/128:
  *     page = block_table[r][b], n = min(128, pos - 128 b + 1),
  *     score[h][t][b] = fl32( sm_scale * max_{s<n} sum_d q[t][h][d] k[page][s][d] ).
@@ -155,24 +201,26 @@ int oracle_block_scores(const uint16_t* q, int64_t q_tok_stride,
                         const void* kdata, const uint8_t* kscales,
                         int64_t num_pages, const int32_t* block_table,
                         int64_t bt_row_stride, const int32_t* seq_lens,
-                        int num_reqs, int query_len, float sm_scale,
-                        float* scores, int64_t s_head_stride,
+                        int num_reqs, int query_len,
+                        const int32_t* cu_seqlens_q, const int32_t* prefix_lens,
+                        float sm_scale, float* scores, int64_t s_head_stride,
                         int64_t s_row_stride, const int64_t* rows,
                         int64_t num_rows)
 {
     static orc_fp4_table table;
     if (kfmt == 1 && !table.ready)
         orc_fp4_table_init(&table);
-    if (query_len <= 0 || heads <= 0)
+    if ((!cu_seqlens_q && query_len <= 0) || heads <= 0)
         return -1;
-    int64_t total = (int64_t)num_reqs * query_len;
+    int64_t total = orc_total_rows(num_reqs, query_len, cu_seqlens_q);
     int64_t n = rows ? num_rows : total;
     for (int64_t i = 0; i < n; ++i) {
         int64_t t = rows ? rows[i] : i;
-        if (t < 0 || t >= total)
+        int r;
+        int64_t pos;
+        if (orc_row(t, seq_lens, num_reqs, query_len, cu_seqlens_q,
+                    prefix_lens, &r, &pos) != 0)
             return -1;
-        int r = (int)(t / query_len), j = (int)(t % query_len);
-        int64_t pos = (int64_t)seq_lens[r] - query_len + j;
         if (pos < 0)
             continue;
         int64_t nv = pos / ORC_BLOCK + 1;
@@ -233,21 +281,24 @@ static int orc_cand_cmp(const void* pa, const void* pb)
  */
 int oracle_topk(const float* scores, int64_t s_head_stride,
                 int64_t s_row_stride, int heads, const int32_t* seq_lens,
-                int num_reqs, int query_len, int topk, int init_blocks,
+                int num_reqs, int query_len, const int32_t* cu_seqlens_q,
+                const int32_t* prefix_lens, int topk, int init_blocks,
                 int local_blocks, int32_t* out, int64_t o_head_stride,
                 int64_t o_row_stride, const int64_t* rows, int64_t num_rows)
 {
     if (topk <= 0 || init_blocks < 0 || local_blocks < 0 ||
-        init_blocks + local_blocks > topk || query_len <= 0)
+        init_blocks + local_blocks > topk || (!cu_seqlens_q && query_len <= 0))
         return -1;
-    int64_t total = (int64_t)num_reqs * query_len;
+    int64_t total = orc_total_rows(num_reqs, query_len, cu_seqlens_q);
     int64_t n = rows ? num_rows : total;
     for (int64_t i = 0; i < n; ++i) {
         int64_t t = rows ? rows[i] : i;
-        if (t < 0 || t >= total)
+        int r;
+        int64_t pos;
+        if (orc_row(t, seq_lens, num_reqs, query_len, cu_seqlens_q,
+                    prefix_lens, &r, &pos) != 0)
             return -1;
-        int r = (int)(t / query_len), j = (int)(t % query_len);
-        int64_t pos = (int64_t)seq_lens[r] - query_len + j;
+        (void)r;
         int64_t nv = pos < 0 ? 0 : pos / ORC_BLOCK + 1;
         char* sel = (char*)calloc(nv > 0 ? (size_t)nv : 1, 1);
         orc_cand* c = (orc_cand*)malloc((nv > 0 ? (size_t)nv : 1) * sizeof *c);
@@ -305,17 +356,21 @@ int oracle_topk(const float* scores, int64_t s_head_stride,
  */
 int oracle_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride,
                               int topk, const int32_t* seq_lens, int num_reqs,
-                              int query_len, const int32_t* abt,
+                              int query_len, const int32_t* cu_seqlens_q,
+                              const int32_t* prefix_lens, const int32_t* abt,
                               int64_t abt_row_stride, int pages_per_block,
                               int block_page_stride, int32_t* sparse,
                               int64_t st_row_stride, int32_t* ctx_lens)
 {
-    if (topk <= 0 || query_len <= 0 || pages_per_block <= 0)
+    if (topk <= 0 || (!cu_seqlens_q && query_len <= 0) || pages_per_block <= 0)
         return -1;
-    int64_t total = (int64_t)num_reqs * query_len;
+    int64_t total = orc_total_rows(num_reqs, query_len, cu_seqlens_q);
     for (int64_t t = 0; t < total; ++t) {
-        int r = (int)(t / query_len), j = (int)(t % query_len);
-        int64_t pos = (int64_t)seq_lens[r] - query_len + j;
+        int r;
+        int64_t pos;
+        if (orc_row(t, seq_lens, num_reqs, query_len, cu_seqlens_q,
+                    prefix_lens, &r, &pos) != 0)
+            return -1;
         int64_t len = 0;
         for (int k = 0; k < topk; ++k) {
             int32_t b = topk_idx[t * o_row_stride + k];

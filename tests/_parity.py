@@ -42,9 +42,26 @@ def _forced(nv, I, L):
     return set(range(min(I, nv))) | set(range(max(0, nv - L), nv))
 
 
-def check_ids(ids_gpu, ids_ref, s_ref, seq_lens, Q, topk, I, L, rows=None):
+def row_positions(seq_lens, Q, cu=None, prefix=None):
+    """Position of every row [T] (int64).  Uniform batches: request r's row j
+    at seq_lens[r] - Q + j.  Ragged: rows cu[r]..cu[r+1]-1, row j at
+    prefix[r] + j, or seq_lens[r] - rows + j without prefix."""
+    seq = np.asarray(seq_lens, dtype=np.int64)
+    if cu is None:
+        t = np.arange(seq.size * Q)
+        return seq[t // Q] - Q + t % Q
+    cu = np.asarray(cu, dtype=np.int64)
+    n = np.diff(cu)
+    first = np.asarray(prefix, dtype=np.int64) if prefix is not None else seq - n
+    req = np.repeat(np.arange(seq.size), n)
+    j = np.arange(int(cu[-1])) - cu[req]
+    return first[req] + j
+
+
+def check_ids(ids_gpu, ids_ref, s_ref, seq_lens, Q, topk, I, L, rows=None, cu=None, prefix=None):
     """ids_* [H, T, topk] int32.  Returns the number of near-tie rows."""
     H = ids_ref.shape[0]
+    pos_all = row_positions(seq_lens, Q, cu, prefix)
     rows = range(ids_ref.shape[1]) if rows is None else rows
     near = 0
     for h in range(H):
@@ -52,7 +69,7 @@ def check_ids(ids_gpu, ids_ref, s_ref, seq_lens, Q, topk, I, L, rows=None):
             g, o = ids_gpu[h, t], ids_ref[h, t]
             if np.array_equal(g, o):
                 continue
-            pos = int(seq_lens[t // Q]) - Q + t % Q
+            pos = int(pos_all[t])
             nv = pos // 128 + 1 if pos >= 0 else 0
             F = _forced(nv, I, L)
             gs = set(int(x) for x in g if x >= 0)
@@ -72,12 +89,12 @@ def check_ids(ids_gpu, ids_ref, s_ref, seq_lens, Q, topk, I, L, rows=None):
     return near
 
 
-def check_invariants(ids, seq_lens, Q, topk, I, L):
+def check_invariants(ids, seq_lens, Q, topk, I, L, cu=None, prefix=None):
     """Every row: ascending distinct ids < nv, trailing -1 only, count =
     min(topk, nv), forced blocks present.  Vectorised over [H, T, topk]."""
     H, T, K = ids.shape
-    t = np.arange(T)
-    pos = seq_lens[t // Q].astype(np.int64) - Q + t % Q
+    pos = row_positions(seq_lens, Q, cu, prefix)
+    assert pos.size == T
     nv = np.where(pos >= 0, pos // 128 + 1, 0)
     cnt = np.minimum(nv, topk)
     valid = ids >= 0
@@ -103,4 +120,5 @@ def check_invariants(ids, seq_lens, Q, topk, I, L):
 def oracle_forward(a, width, topk, I, L, rows=None):
     return oracle.forward(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
                           a["seq_lens"], a["query_len"], a["sm_scale"], topk, I, L, width,
-                          rows=rows)
+                          rows=rows, cu_seqlens_q=a.get("cu_seqlens_q"),
+                          prefix_lens=a.get("prefix_lens"))

@@ -193,3 +193,106 @@ def test_short_requests_have_no_rows():
     got = _oracle_scores(a, w.score_width)
     assert np.isnan(got[0, [0, 1, 4, 5, 6, 7]]).all()
     assert not np.isnan(got[0, [2, 3], 0]).any()
+
+
+# ---------------------------------------------------------------- ragged
+#
+# Ragged batches (page "ops.index_topk", minimax_m3_index_score signature:
+# cu_seqlens_q row offsets and prefix_lens).  Request r owns rows
+# cu[r]..cu[r+1]-1; its row j sits at prefix_lens[r] + j, or at
+# seq_lens[r] - rows + j when no prefix_lens are given.
+
+def _ragged_positions(a):
+    seq = a["seq_lens"].astype(np.int64)
+    cu = a["cu_seqlens_q"].astype(np.int64)
+    out = []
+    for r in range(seq.size):
+        n = int(cu[r + 1] - cu[r])
+        p0 = int(a["prefix_lens"][r]) if a["prefix_lens"] is not None else int(seq[r]) - n
+        out += [(r, int(cu[r]) + j, p0 + j) for j in range(n)]
+    return out
+
+
+def brute_scores_ragged(a, width):
+    """The numpy float64 pin above, with rows and positions from the ragged
+    batch description."""
+    q = _bf16_to_f64(a["q_bits"])
+    T, H, _ = q.shape
+    out = np.full((H, T, width), np.nan, dtype=np.float32)
+    for r, t, pos in _ragged_positions(a):
+        if pos < 0:
+            continue
+        nv = pos // 128 + 1
+        K = _keys_f64(a, a["block_table"][r, :nv]).reshape(nv * 128, 128)
+        dots = q[t] @ K.T
+        dots[:, pos + 1:] = -np.inf
+        out[:, t, :nv] = (a["sm_scale"] * dots.reshape(H, nv, 128).max(-1)).astype(np.float32)
+    return out
+
+
+def _ragged_small(seed, kfmt=KFMT_BF16, prefix=None, qlens=(3, 0, 1, 7, 2), H=2, msl=1024,
+                  lens=(1, 900)):
+    return make(name="t", R=len(qlens), lens=lens, Q=8, H=H, max_seq_len=msl, topk=4, I=1, L=1,
+                kfmt=kfmt, seed=seed, device="cpu", qlens=list(qlens), prefix=prefix)
+
+
+def _oracle_ragged(a, width, rows=None):
+    return oracle.block_scores(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"],
+                               a["block_table"], a["seq_lens"], a["query_len"],
+                               a["sm_scale"], width, rows=rows,
+                               cu_seqlens_q=a["cu_seqlens_q"], prefix_lens=a["prefix_lens"])
+
+
+@pytest.mark.parametrize("prefix", [None, "tail", "gap"])
+@pytest.mark.parametrize("kfmt", [KFMT_BF16, KFMT_NVFP4])
+def test_ragged_vs_numpy_float64(kfmt, prefix):
+    w = _ragged_small(21, kfmt=kfmt, prefix=prefix)
+    a = host_arrays(w)
+    assert a["cu_seqlens_q"].tolist()[-1] == w.rows
+    _same(_oracle_ragged(a, w.score_width), brute_scores_ragged(a, w.score_width),
+          rtol=1e-6, atol=1e-6)
+
+
+def test_ragged_gap_keys_are_invisible():
+    """With prefix_lens below seq_len - rows, the keys after the last row's
+    position hold poison (a huge value); no score may see it."""
+    w = _ragged_small(22, prefix="gap", qlens=(5, 8, 2), lens=(300, 900))
+    a = host_arrays(w)
+    assert (a["prefix_lens"] + np.diff(a["cu_seqlens_q"]) < a["seq_lens"]).any()
+    got = _oracle_ragged(a, w.score_width)
+    assert np.nanmax(np.abs(got)) < 100.0
+
+
+def test_ragged_equals_requests_alone():
+    """A ragged batch scores each request as a uniform one-request batch with
+    query_len = its rows and seq_len = its last row's position + 1."""
+    w = _ragged_small(23, prefix="gap", qlens=(4, 1, 6, 0, 3))
+    a = host_arrays(w)
+    full = _oracle_ragged(a, w.score_width)
+    cu = a["cu_seqlens_q"]
+    for r in range(a["seq_lens"].size):
+        n = int(cu[r + 1] - cu[r])
+        if n == 0:
+            continue
+        end = int(a["prefix_lens"][r]) + n
+        alone = oracle.block_scores(a["q_bits"][cu[r]:cu[r + 1]], a["kfmt"], a["kdata"],
+                                    a["kscales"], a["block_table"][r:r + 1],
+                                    np.array([end], dtype=np.int32), n, a["sm_scale"],
+                                    w.score_width)
+        _same(full[:, cu[r]:cu[r + 1]], alone)
+
+
+def test_ragged_rows_subset_matches_full():
+    w = _ragged_small(24, prefix="tail")
+    a = host_arrays(w)
+    full = _oracle_ragged(a, w.score_width)
+    rows = [0, 3, 4, 10]
+    sub = _oracle_ragged(a, w.score_width, rows=rows)
+    _same(sub[:, rows], full[:, rows])
+
+
+def test_ragged_rejects_rows_outside_the_batch():
+    w = _ragged_small(25)
+    a = host_arrays(w)
+    with pytest.raises(ValueError):
+        _oracle_ragged(a, w.score_width, rows=[w.rows])

@@ -146,3 +146,45 @@ def test_sparse_block_table_hand_worked():
     sp, ctx = oracle.sparse_block_table(ids, seq, 1, abt, 2, 2)
     assert sp.tolist() == [[10, 11, 20, 21, 22, 23, -1, -1]]
     assert ctx.tolist() == [266]
+
+
+# ------------------------------------------------------------ ragged rows
+
+def test_ragged_rows_select_by_their_own_position():
+    """Ragged batch (cu_seqlens_q, prefix_lens): each row selects as a
+    single-row problem whose position is prefix + j."""
+    rng = np.random.default_rng(7)
+    seq = np.array([3000, 700, 5000], dtype=np.int32)
+    cu = np.array([0, 2, 2, 7], dtype=np.int32)  # request 1 has no rows
+    pre = np.array([1500, 0, 4000], dtype=np.int32)
+    T, W = 7, 48
+    s = rng.integers(-8, 8, size=(1, T, W)).astype(np.float32)
+    got = oracle.topk(s, seq, 5, 6, 1, 2, cu_seqlens_q=cu, prefix_lens=pre)
+    for r in range(3):
+        for j in range(cu[r + 1] - cu[r]):
+            t = cu[r] + j
+            nv = (int(pre[r]) + j) // 128 + 1
+            _check_row(got[0, t], s[0, t], nv, 6, 1, 2)
+            assert got[0, t].tolist() == _one_row(s[0, t, :nv], 6, 1, 2).tolist()
+
+
+def test_ragged_without_prefix_uses_the_last_tokens():
+    s = np.zeros((1, 3, 16), dtype=np.float32)
+    seq = np.array([129, 1], dtype=np.int32)
+    cu = np.array([0, 2, 3], dtype=np.int32)
+    # request 0: rows at positions 127, 128 (nv 1, 2); request 1: position 0
+    got = oracle.topk(s, seq, 2, 4, 0, 0, cu_seqlens_q=cu)
+    assert got[0].tolist() == [[0, -1, -1, -1], [0, 1, -1, -1], [0, -1, -1, -1]]
+
+
+def test_ragged_sparse_table_context_lengths():
+    abt = np.arange(100, 140, dtype=np.int32).reshape(2, 20)
+    seq = np.array([1000, 300], dtype=np.int32)
+    cu = np.array([0, 1, 3], dtype=np.int32)
+    pre = np.array([260, 129], dtype=np.int32)
+    ids = np.array([[0, 2, -1], [0, 1, -1], [1, -1, -1]], dtype=np.int32)
+    sp, ctx = oracle.sparse_block_table(ids, seq, 2, abt, 1, 1, cu_seqlens_q=cu, prefix_lens=pre)
+    assert sp.tolist() == [[100, 102, -1], [120, 121, -1], [121, -1, -1]]
+    # row 0 at 260: block 0 full, block 2 holds 260-256+1 = 5; row 1 at 129:
+    # 128 + 2; row 2 at 130: block 1 holds 3
+    assert ctx.tolist() == [133, 130, 3]

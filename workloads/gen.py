@@ -9,7 +9,9 @@ returns; neither imports the other.
 Shapes follow the pages: queries [tokens, heads, 128] bf16, index-K pages
 [pages, 128, 128] bf16 with one page per 128-token block, int32 block table
 and lengths, query_len rows per request (page "ops.index_topk", module
-docstring; page "indexer_context_parallel", check_context_score_inputs).
+docstring; page "indexer_context_parallel", check_context_score_inputs), or
+ragged batches with cu_seqlens_q row offsets and optional prefix_lens (page
+"ops.index_topk", minimax_m3_index_score signature).
 NVFP4 keys are e2m1 nibbles with one e4m3 scale per 16 elements (page
 "indexer_nvfp4", module docstring).
 """
@@ -44,12 +46,25 @@ class Workload:
     kscales: Optional[torch.Tensor]  # uint8 [P,128,8] or None
     block_table: torch.Tensor  # int32 [R, W]
     seq_lens: torch.Tensor  # int32 [R]
-    query_len: int
+    query_len: int  # rows per request; ragged: the bound on every request's rows
     max_seq_len: int
     sm_scale: float
     topk: int
     init_blocks: int
     local_blocks: int
+    cu_seqlens_q: Optional[torch.Tensor] = None  # int32 [R+1] (ragged batches)
+    prefix_lens: Optional[torch.Tensor] = None  # int32 [R] (position of a request's first row)
+
+    @property
+    def ragged(self) -> bool:
+        return self.cu_seqlens_q is not None
+
+    def row_ranges(self):
+        """[(first row, rows)] per request (host ints)."""
+        if self.cu_seqlens_q is None:
+            return [(r * self.query_len, self.query_len) for r in range(self.num_reqs)]
+        cu = self.cu_seqlens_q.detach().cpu().tolist()
+        return [(cu[r], cu[r + 1] - cu[r]) for r in range(self.num_reqs)]
 
     @property
     def num_reqs(self) -> int:
@@ -78,7 +93,8 @@ class Workload:
         f = lambda t: None if t is None else t.to(device)
         return dataclasses.replace(
             self, q=f(self.q), kdata=f(self.kdata), kscales=f(self.kscales),
-            block_table=f(self.block_table), seq_lens=f(self.seq_lens))
+            block_table=f(self.block_table), seq_lens=f(self.seq_lens),
+            cu_seqlens_q=f(self.cu_seqlens_q), prefix_lens=f(self.prefix_lens))
 
 
 def cdiv(a: int, b: int) -> int:
@@ -147,12 +163,22 @@ def _quantize_nvfp4(x: torch.Tensor):
 
 def make(name, R, lens, Q, H, max_seq_len, topk, I, L, kfmt, seed, device,
          pool=None, dup_frac=0.0, block_sigma=0.0, fixed_lens=None,
-         sm_scale=None, poison=True, chunk_pages=4096) -> Workload:
+         sm_scale=None, poison=True, chunk_pages=4096, qlens=None,
+         prefix=None, max_gap=300) -> Workload:
     """Draw one workload.  Lengths ~ U[lens[0], lens[1]] (integers); pages
     are a seeded random permutation of a pool of sum(cdiv(len,128)) pages
     (plus one page that only the unused block-table entries point at);
     q, k ~ N(0,1) rounded to bf16; NVFP4 keys are N(0,1) values encoded by
-    _quantize_nvfp4."""
+    _quantize_nvfp4.
+
+    Ragged batches: qlens gives each request's row count, as a list or as a
+    (lo, hi) range drawn uniformly per request; Q is then the bound on them
+    (cu_seqlens_q holds the row offsets).  prefix: None (no prefix_lens: a
+    request's rows are its last tokens), "tail" (prefix_lens = seq_len -
+    rows, passed explicitly) or "gap" (prefix_lens = seq_len - rows - gap,
+    gap ~ U[0, max_gap]: the keys after the last row's position exist but no
+    row sees them; they are poisoned).  With a prefix, rows are capped at
+    seq_len."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(int(seed))
@@ -164,6 +190,31 @@ def make(name, R, lens, Q, H, max_seq_len, topk, I, L, kfmt, seed, device,
         seq = torch.randint(lens[0], lens[1] + 1, (R,), generator=g, device=dev)
     seq_host = seq.cpu().tolist()
     assert max(seq_host + [0]) <= max_seq_len
+    cu = pre = None
+    if qlens is not None:
+        if isinstance(qlens, tuple):
+            nq = torch.randint(qlens[0], qlens[1] + 1, (R,), generator=g, device=dev).cpu().tolist()
+        else:
+            nq = [int(x) for x in qlens]
+            assert len(nq) == R
+        if prefix is not None:
+            nq = [min(n, s) for n, s in zip(nq, seq_host)]
+        assert max(nq + [0]) <= Q
+        cu_host = [0]
+        for n in nq:
+            cu_host.append(cu_host[-1] + n)
+        cu = torch.tensor(cu_host, dtype=torch.int32, device=dev)
+        if prefix is not None:
+            assert prefix in ("tail", "gap")
+            gaps = [0] * R
+            if prefix == "gap":
+                gaps = torch.randint(0, max_gap + 1, (R,), generator=g, device=dev).cpu().tolist()
+            pre_host = [max(0, s - n - gp) for s, n, gp in zip(seq_host, nq, gaps)]
+            pre = torch.tensor(pre_host, dtype=torch.int32, device=dev)
+        T = cu_host[-1]
+    else:
+        assert prefix is None and Q >= 1
+        T = R * Q
     nblk = [cdiv(s, BLOCK) for s in seq_host]
     used = sum(nblk)
     npages = max(used + 1, pool or 0)
@@ -178,7 +229,7 @@ def make(name, R, lens, Q, H, max_seq_len, topk, I, L, kfmt, seed, device,
         for r, nb in enumerate(nblk):
             bt[r, :nb] = perm[off:off + nb]
             off += nb
-    q = torch.randn((R * Q, H, DIM), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((T, H, DIM), generator=g, device=dev).to(torch.bfloat16)
 
     # K pool, drawn in chunks of pages to bound the fp32 temporary
     if kfmt == KFMT_BF16:
@@ -215,13 +266,21 @@ def make(name, R, lens, Q, H, max_seq_len, topk, I, L, kfmt, seed, device,
                 page = int(bt_host[r, nblk[r] - 1])
                 _fill_poison(kdata, kscales, torch.tensor([page], device=dev),
                              slice(tail, BLOCK))
+        if pre is not None:
+            # keys after the last row's position: present, seen by no row
+            for r, (p0, s) in enumerate(zip(pre.cpu().tolist(), seq_host)):
+                end = p0 + cu_host[r + 1] - cu_host[r]
+                for p in range(end, s):
+                    page = int(bt_host[r, p // BLOCK])
+                    _fill_poison(kdata, kscales, torch.tensor([page], device=dev),
+                                 slice(p % BLOCK, p % BLOCK + 1))
 
     return Workload(
         name=name, q=q, kfmt=kfmt, kdata=kdata, kscales=kscales,
         block_table=bt, seq_lens=seq.to(torch.int32), query_len=Q,
         max_seq_len=max_seq_len,
         sm_scale=float(1.0 / math.sqrt(DIM)) if sm_scale is None else float(sm_scale),
-        topk=topk, init_blocks=I, local_blocks=L)
+        topk=topk, init_blocks=I, local_blocks=L, cu_seqlens_q=cu, prefix_lens=pre)
 
 
 def _fill_poison(kdata, kscales, pages, toks):
@@ -263,10 +322,12 @@ def host_arrays(w: Workload):
     else:
         kd = w.kdata.detach().cpu().contiguous().numpy()
         ks = w.kscales.detach().cpu().contiguous().numpy()
+    f = lambda t: None if t is None else t.detach().cpu().numpy()
     return dict(q_bits=q, kfmt=w.kfmt, kdata=kd, kscales=ks,
                 block_table=w.block_table.detach().cpu().numpy(),
                 seq_lens=w.seq_lens.detach().cpu().numpy(),
-                query_len=w.query_len, sm_scale=w.sm_scale)
+                query_len=w.query_len, sm_scale=w.sm_scale,
+                cu_seqlens_q=f(w.cu_seqlens_q), prefix_lens=f(w.prefix_lens))
 
 
 def host_subset(w: Workload, reqs, max_pages_per_req=None):
@@ -276,6 +337,7 @@ def host_subset(w: Workload, reqs, max_pages_per_req=None):
     the subset's rows back to rows of the full workload."""
     reqs = [int(r) for r in reqs]
     Q = w.query_len
+    ranges = w.row_ranges()
     seq = w.seq_lens.detach().cpu()
     bt = w.block_table.detach().cpu()
     pages, tables = [], []
@@ -291,7 +353,8 @@ def host_subset(w: Workload, reqs, max_pages_per_req=None):
         nbt[i, :t.numel()] = inv[off:off + t.numel()].to(torch.int32)
         off += t.numel()
     dev_idx = uniq.to(w.kdata.device)
-    rows = torch.cat([torch.arange(r * Q, (r + 1) * Q) for r in reqs]) if reqs else torch.zeros(0, dtype=torch.long)
+    rows = (torch.cat([torch.arange(ranges[r][0], ranges[r][0] + ranges[r][1]) for r in reqs])
+            if reqs else torch.zeros(0, dtype=torch.long))
     q = w.q.index_select(0, rows.to(w.q.device)).cpu().contiguous()
     q = q.view(torch.int16).numpy().view(np.uint16)
     if w.kfmt == KFMT_BF16:
@@ -300,7 +363,12 @@ def host_subset(w: Workload, reqs, max_pages_per_req=None):
     else:
         kd = w.kdata.index_select(0, dev_idx).cpu().contiguous().numpy()
         ks = w.kscales.index_select(0, dev_idx).cpu().contiguous().numpy()
+    cu = pre = None
+    if w.ragged:
+        cu = np.cumsum([0] + [ranges[r][1] for r in reqs]).astype(np.int32)
+        if w.prefix_lens is not None:
+            pre = w.prefix_lens.detach().cpu().numpy()[reqs].astype(np.int32)
     arrays = dict(q_bits=q, kfmt=w.kfmt, kdata=kd, kscales=ks,
                   block_table=nbt.numpy(), seq_lens=seq[reqs].numpy().astype(np.int32),
-                  query_len=Q, sm_scale=w.sm_scale)
+                  query_len=Q, sm_scale=w.sm_scale, cu_seqlens_q=cu, prefix_lens=pre)
     return arrays, rows.numpy()
