@@ -4,7 +4,9 @@
 One step = the whole hot path over one batch of synthetic input already
 resident in HBM: the decode scorer (paged-K gather + MFMA GEMV + causal block
 max) and the top-k selector, as one mm3_index_decode call (workloads 1, 2, 3,
-5), or mm3_index_score then mm3_index_topk (chunked prefill, workload 4).
+5), or mm3_index_score then mm3_index_topk (chunked prefill, workloads 4 and
+6; the ragged serving batch, workload 7, whose decode requests and prefill
+chunks share one call).
 
 Default workload: the 64-request decode batch (seq_len ~ U[4096, 32768],
 query_len 4, 4 index heads, topk 16, 1 init + 2 local blocks).
@@ -38,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--copies", type=int, default=2, help="page-pool copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -82,26 +84,40 @@ def recorded_traffic(workload: str, kernel: str):
 
 
 def algorithmic(w, seq):
-    """Algorithmic bytes (decode) and flops (prefill) of one pass."""
+    """Algorithmic work of one pass.  Requests with heads * rows <= 16 go to
+    the decode scorer, whose unit is bytes: every visible key once, the query
+    rows, the block-table entries and the scores written.  Larger ones go to
+    the prefill scorer, whose unit is flops: 2 * 128 per (row, head, visible
+    key).  A request's visible keys are those up to its last row."""
     import numpy as np
-    Q, H, k = w.query_len, w.heads, w.topk
-    T = w.rows
-    t = np.arange(T)
-    pos = seq[t // Q].astype(np.int64) - Q + t % Q
-    nv = np.where(pos >= 0, pos // 128 + 1, 0)
+    H, k = w.heads, w.topk
     key_b = w.key_bytes_per_token()
-    kbytes = int(seq.astype(np.int64).sum()) * key_b
-    qbytes = T * H * 256
-    tbytes = int(np.ceil(seq / 128).sum()) * 4
+    pre = w.prefix_lens.cpu().numpy() if w.prefix_lens is not None else None
+    dec = dict(k=0, q=0, t=0, s=0)
+    flops = tokens = pairs = 0
+    nv_all = []
+    for r, (_, n) in enumerate(w.row_ranges()):
+        p0 = int(pre[r]) if pre is not None else int(seq[r]) - n
+        pos = p0 + np.arange(n, dtype=np.int64)
+        nv = np.where(pos >= 0, pos // 128 + 1, 0)
+        nv_all.append(nv)
+        vis = max(0, p0 + n)
+        tokens += vis
+        pairs += H * int((pos + 1).clip(0).sum())
+        if H * n <= 16:
+            dec["k"] += vis * key_b
+            dec["q"] += n * H * 256
+            dec["t"] += -(-vis // 128) * 4
+            dec["s"] += H * int(nv.sum()) * 4
+        else:
+            flops += 2 * 128 * H * int((pos + 1).clip(0).sum())
+    nv = np.concatenate(nv_all) if nv_all else np.zeros(0, np.int64)
+    T = w.rows
     score_bytes = H * int(nv.sum()) * 4
     out_bytes = H * T * k * 4
-    flops = 2 * 128 * H * int((pos + 1).clip(0).sum())
-    scorer = kbytes + qbytes + tbytes + score_bytes
-    return dict(k_bytes=kbytes, scorer_bytes=scorer,
-                step_bytes=kbytes + qbytes + tbytes + out_bytes,
-                selector_bytes=score_bytes + out_bytes, flops=flops,
-                tokens=int(seq.astype(np.int64).sum()), rows=H * T,
-                pairs=H * int((pos + 1).clip(0).sum()))
+    scorer = dec["k"] + dec["q"] + dec["t"] + dec["s"]
+    return dict(k_bytes=dec["k"], scorer_bytes=scorer, selector_bytes=score_bytes + out_bytes,
+                flops=flops, tokens=tokens, rows=H * T, pairs=pairs)
 
 
 def main():
@@ -136,13 +152,14 @@ def main():
             q=base.q.clone(), block_table=base.block_table.clone(),
             seq_lens=base.seq_lens.clone()))
     prefill = base.heads * base.query_len > 16
+    rg = lambda w: dict(cu_seqlens_q=w.cu_seqlens_q, prefix_lens=w.prefix_lens)
     H, T = base.heads, base.rows
     outs = [torch.empty((H, T, base.topk), dtype=torch.int32, device=dev) for _ in copies]
     scores = [torch.empty((H, T, base.score_width), dtype=torch.float32, device=dev) for _ in copies]
     wss = []
     for w in copies:
         p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
-                             w.sm_scale, w.kscales)
+                             w.sm_scale, w.kscales, **rg(w))
         n = mm3.decode_workspace_bytes(p, w.topk, False)
         wss.append(torch.empty(max(n, 256), dtype=torch.uint8, device=dev))
 
@@ -151,26 +168,27 @@ def main():
         w = copies[c]
         if prefill:
             mm3.mm3_index_score(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
-                                w.max_seq_len, w.sm_scale, kscales=w.kscales, scores=scores[c])
+                                w.max_seq_len, w.sm_scale, kscales=w.kscales, scores=scores[c],
+                                **rg(w))
             mm3.mm3_index_topk(scores[c], w.seq_lens, w.query_len, w.max_seq_len, w.topk,
-                               w.init_blocks, w.local_blocks, out=outs[c])
+                               w.init_blocks, w.local_blocks, out=outs[c], **rg(w))
         else:
             mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
                                  w.max_seq_len, w.sm_scale, w.topk, w.init_blocks,
                                  w.local_blocks, kscales=w.kscales, out=outs[c],
-                                 workspace=wss[c])
+                                 workspace=wss[c], **rg(w))
 
     def score_only(i):
         c = i % len(copies)
         w = copies[c]
         mm3.mm3_index_score(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
-                            w.sm_scale, kscales=w.kscales, scores=scores[c])
+                            w.sm_scale, kscales=w.kscales, scores=scores[c], **rg(w))
 
     def topk_only(i):
         c = i % len(copies)
         w = copies[c]
         mm3.mm3_index_topk(scores[c], w.seq_lens, w.query_len, w.max_seq_len, w.topk,
-                           w.init_blocks, w.local_blocks, out=outs[c])
+                           w.init_blocks, w.local_blocks, out=outs[c], **rg(w))
 
     def timed(fn, n, warm):
         for i in range(warm):
@@ -215,7 +233,21 @@ def main():
     alg = algorithmic(base, seq)
     tokens_per_s = alg["tokens"] / (ms * 1e-3)
     rows_per_s = alg["rows"] / (ms * 1e-3)
-    if prefill:
+    if prefill and alg["scorer_bytes"]:
+        # decode requests and prefill chunks in one call: both scorers run.
+        # The bound is the time the two would take at peak (bytes at HBM
+        # peak plus flops at MFMA peak), expressed in the dominant unit.
+        t_hbm = alg["scorer_bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = alg["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        frac = (t_hbm + t_mfma) / (ms_score * 1e-3)
+        roof = dict(bound="mfma", achieved=round(frac * BF16_MFMA_PEAK_TFLOPS, 2),
+                    peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s", frac=round(frac, 4),
+                    traffic=None,
+                    kernel="decode_score_cu<%d> + prefill_score_kernel<%d, true>" % (base.kfmt, base.kfmt),
+                    ms=round(ms_score, 4), per_launch_flops=alg["flops"],
+                    per_launch_bytes=alg["scorer_bytes"],
+                    combined="(bytes/8 TB/s + flops/2.5 PFLOP/s) / measured time, over both scorers")
+    elif prefill:
         achieved = alg["flops"] / (ms_score * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -254,7 +286,8 @@ def main():
             "num_reqs": base.num_reqs,
             "seq_len_range": list(cfg["lens"]),
             "sum_seq_len": alg["tokens"],
-            "query_len": base.query_len,
+            "query_len": base.query_len if not base.ragged else "ragged, max %d" % base.query_len,
+            "rows": base.rows,
             "index_heads": base.heads,
             "head_dim": 128,
             "block": 128,
@@ -349,21 +382,26 @@ def cpu_baseline(w, seq, seconds):
     # estimate from the first request, then take as many as fit
     done, tok, el = [], 0, 0.0
     budget = seconds
+    ranges = w.row_ranges()
+    sampled = False
     for r in order:
+        n = ranges[r][1]
+        if n == 0:
+            continue
         a, rows = host_subset(w, [r])
         rows_loc = None
-        if w.query_len > 64:  # prefill: a bounded sample of rows per request
-            rows_loc = list(range(0, w.query_len, max(1, w.query_len // 16)))
+        if n > 64:  # prefill: a bounded sample of rows per request
+            rows_loc = list(range(0, n, max(1, n // 16)))
+            sampled = True
         t0 = time.perf_counter()
         oracle.forward(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
                        a["seq_lens"], a["query_len"], a["sm_scale"], w.topk, w.init_blocks,
-                       w.local_blocks, w.score_width, rows=rows_loc)
+                       w.local_blocks, w.score_width, rows=rows_loc,
+                       cu_seqlens_q=a["cu_seqlens_q"], prefix_lens=a["prefix_lens"])
         el += time.perf_counter() - t0
-        nrows = w.query_len if rows_loc is None else len(rows_loc)
-        if w.query_len > 64:
-            tok += int(seq[r]) * nrows / w.query_len  # tokens-equivalent of sampled rows
-        else:
-            tok += int(seq[r])
+        nrows = n if rows_loc is None else len(rows_loc)
+        vis = (int(a["prefix_lens"][0]) + n) if a["prefix_lens"] is not None else int(seq[r])
+        tok += vis * nrows / n  # tokens-equivalent of the rows done
         done.append(r)
         if el >= budget:
             break
@@ -373,7 +411,7 @@ def cpu_baseline(w, seq, seconds):
         "cores": 1,
         "kind": "oracle",
         "sample": (f"{len(done)} of {w.num_reqs} requests" +
-                   (" (every %d-th row)" % max(1, w.query_len // 16) if w.query_len > 64 else "") +
+                   (" (about 16 rows of each request over 64 rows)" if sampled else "") +
                    f", {int(tok)} tokens, {el:.1f} s, single-threaded fp64 C oracle"),
         "host_cpus": os.cpu_count(),
     }

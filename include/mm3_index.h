@@ -18,10 +18,15 @@
  * score as e4m3_rn_satfinite(e2m1 * scale)).
  *
  * Conventions shared by every entry point
- *  - Rows.  Request r owns rows t = r*query_len + j, j < query_len
- *    (tokens == num_reqs * query_len, request-major).  Row t sits at
- *    position pos = seq_lens[r] - query_len + j and sees the nv = pos/128 + 1
- *    blocks b <= pos/128; in block b it sees tokens 128*b + s <= pos.  Rows
+ *  - Rows (struct mm3_rows).  Uniform batches: request r owns rows
+ *    t = r*query_len + j, j < query_len, and row j sits at position
+ *    pos = seq_lens[r] - query_len + j.  Ragged batches (cu_seqlens_q given;
+ *    page "ops.index_topk", minimax_m3_index_score and minimax_m3_index_topk
+ *    signatures): request r owns rows cu_seqlens_q[r] <= t <
+ *    cu_seqlens_q[r+1], and its row j sits at prefix_lens[r] + j, or, without
+ *    prefix_lens, at seq_lens[r] - n_r + j (n_r = its row count: the chunk is
+ *    the request's last n_r tokens).  A row at pos sees the nv = pos/128 + 1
+ *    blocks b <= pos/128 and in block b the tokens 128*b + s <= pos.  Rows
  *    with pos < 0 see nothing.
  *  - Pointers are DEVICE pointers unless a parameter says "host".  The
  *    mm3_problem struct itself is read on the host during the call only.
@@ -35,9 +40,9 @@
  *    after a call returns.
  *  - Errors: every host-checkable rule is checked before anything is
  *    enqueued; a non-zero return leaves every output untouched.
- *    mm3_last_error() then describes it (thread-local).  Device VALUES are
- *    preconditions, not checked: 0 <= seq_lens[r] <= max_seq_len and page
- *    ids in [0, num_pages) for every visible block.
+ *    mm3_last_error() then describes it (thread-local).  Device VALUES
+ *    (lengths, row offsets, prefixes, page ids) are preconditions, listed
+ *    with mm3_rows and mm3_problem, and not checked.
  */
 #ifndef MM3_INDEX_H
 #define MM3_INDEX_H
@@ -70,6 +75,34 @@ extern "C" {
 #define MM3_MAX_TOPK 1024
 
 /*
+ * How rows map to requests and positions (see "Rows" above).
+ *   seq_lens     int32 [num_reqs], contiguous; each in [0, max_seq_len].
+ *   cu_seqlens_q NULL (uniform batch), or int32 [num_reqs + 1], contiguous:
+ *                cu[0] == 0, non-decreasing, every n_r = cu[r+1] - cu[r] <=
+ *                query_len, cu[num_reqs] == total_q.
+ *   prefix_lens  NULL, or (ragged batches only) int32 [num_reqs], contiguous:
+ *                prefix_lens[r] >= 0 and prefix_lens[r] + n_r <= seq_lens[r].
+ *   num_reqs     >= 0.
+ *   query_len    >= 1: rows per request; with cu_seqlens_q, a bound on every
+ *                n_r (the pages' max_query_len), which sizes grids.
+ *   total_q      rows in all (tokens); == num_reqs * query_len without
+ *                cu_seqlens_q.  Below 2^31, as is heads * query_len.
+ *   max_seq_len  capture-stable bound on every seq_lens[r] (e.g. the model's
+ *                maximum length, not the batch maximum); sizes the grids.
+ * The arrays live on the device and their VALUES are preconditions, not
+ * checked: values outside these ranges make the kernels read out of bounds.
+ */
+typedef struct mm3_rows {
+    const int32_t* seq_lens;
+    const int32_t* cu_seqlens_q;
+    const int32_t* prefix_lens;
+    int32_t num_reqs;
+    int32_t query_len;
+    int32_t total_q;
+    int32_t max_seq_len;
+} mm3_rows;
+
+/*
  * The scoring problem (page "ops.index_topk", minimax_m3_index_decode and
  * minimax_m3_index_score signatures; page "indexer_context_parallel",
  * check_context_score_inputs).
@@ -79,16 +112,10 @@ extern "C" {
  *   kfmt/kdata/kscales/num_pages  the page pool (formats above), 16-byte
  *                aligned, num_pages >= 1; kscales NULL for bf16.
  *   block_table  int32, entry (r, b) at block_table[r*bt_row_stride + b];
- *                bt_width >= cdiv(max_seq_len, 128); bt_row_stride >= bt_width.
- *   seq_lens     int32 [num_reqs], contiguous; each in [0, max_seq_len], and
- *                block_table entries (r, b < cdiv(seq_lens[r], 128)) in
- *                [0, num_pages).  Both live on the device and are not checked:
- *                values outside these ranges make the kernels read out of
- *                bounds.
- *   query_len    rows per request, >= 1; num_reqs * query_len and
- *                heads * query_len below 2^31.
- *   max_seq_len  capture-stable bound on every seq_lens[r] (e.g. the model's
- *                maximum length, not the batch maximum); sizes the grids.
+ *                bt_width >= cdiv(rows.max_seq_len, 128); bt_row_stride >=
+ *                bt_width.  Entries of every visible block must lie in
+ *                [0, num_pages) (a device precondition, not checked).
+ *   rows         the batch's rows (struct above); q holds rows.total_q tokens.
  *   sm_scale     finite, > 0.
  */
 typedef struct mm3_problem {
@@ -103,11 +130,8 @@ typedef struct mm3_problem {
     const int32_t* block_table;
     int64_t bt_row_stride;
     int32_t bt_width;
-    const int32_t* seq_lens;
-    int32_t num_reqs;
-    int32_t query_len;
-    int32_t max_seq_len;
     float sm_scale;
+    mm3_rows rows;
 } mm3_problem;
 
 /*
@@ -116,15 +140,16 @@ typedef struct mm3_problem {
  * causally visible 128-token block, the block's largest scaled dot product.
  *   scores  fp32, element (h, t, b) at scores[h*s_head_stride + t*s_row_stride + b],
  *           s_width >= cdiv(max_seq_len,128) columns per row,
- *           s_row_stride >= s_width, s_head_stride >= tokens*s_row_stride.
+ *           s_row_stride >= s_width, s_head_stride >= total_q*s_row_stride.
  *           Written: every visible (h, t, b); nothing else is touched.
  *   score = fl32(sm_scale * max over visible tokens of the fp32-accumulated
  *           dot product of q[t, h, :] and the key).
- * Rows with H*query_len <= 16 per request use the bandwidth-bound decode
- * scorer; larger ones the MFMA prefill scorer.  Both take either key format
- * (the prefill scorer decodes each NVFP4 page once into bf16 in LDS).  q and
- * keys are expected finite: a score whose block holds a NaN or infinite
- * product is unspecified.
+ * A request with heads * n_r <= 16 rows is scored by the bandwidth-bound
+ * decode scorer, a larger one by the MFMA prefill scorer; a ragged batch may
+ * mix both kinds in one call.  Both take either key format (the prefill
+ * scorer decodes each NVFP4 page once into bf16 in LDS).  q and keys are
+ * expected finite: a score whose block holds a NaN or infinite product is
+ * unspecified.
  */
 int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
                     int64_t s_row_stride, int32_t s_width, void* stream);
@@ -137,16 +162,16 @@ int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
  *   With F = [0, min(I,nv)) U [max(0,nv-L), nv):
  *     nv <= topk -> ids 0..nv-1;  else F plus the topk-|F| best other blocks
  *     by (score descending, id ascending; -0 == +0).
+ *   rows as in mm3_problem (the same batch the scores were computed for).
  *   out int32, row (h, t) at out[h*o_head_stride + t*o_row_stride], written in
- *   place: the selected ids ascending, then -1 up to topk.  Rows t >= tokens
+ *   place: the selected ids ascending, then -1 up to topk.  Rows t >= total_q
  *   are not touched (stable address for graph capture).
  *   1 <= topk <= 1024, 0 <= I, 0 <= L, I + L <= topk,
- *   o_row_stride >= topk, o_head_stride >= tokens*o_row_stride.
+ *   o_row_stride >= topk, o_head_stride >= total_q*o_row_stride.
  */
 int mm3_index_topk(const float* scores, int64_t s_head_stride,
                    int64_t s_row_stride, int32_t s_width, int32_t heads,
-                   const int32_t* seq_lens, int32_t num_reqs, int32_t query_len,
-                   int32_t max_seq_len, int32_t topk, int32_t init_blocks,
+                   const mm3_rows* rows, int32_t topk, int32_t init_blocks,
                    int32_t local_blocks, int32_t* out, int64_t o_head_stride,
                    int64_t o_row_stride, void* stream);
 
@@ -183,6 +208,7 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
  * sparse_context_lens_out / block_page_stride arguments).
  *   topk_idx   int32 row t at topk_idx[t*o_row_stride], ids as mm3_index_topk
  *              writes them (ascending, -1 padded).
+ *   rows       the batch's rows, as in mm3_problem.
  *   attention_block_table  int32, request r's row at abt[r*abt_row_stride];
  *              sparse block b owns entries [b*block_page_stride,
  *              b*block_page_stride + pages_per_block);
@@ -191,13 +217,11 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
  *   sparse_table int32, row t at sparse_table[t*st_row_stride], st_row_stride
  *              >= topk*P: slot j*P+i = abt[r][b_j*stride + i] for the j-th id,
  *              -1 for slots of -1 ids.
- *   sparse_ctx_lens int32 [tokens]: sum over selected b of the visible tokens
+ *   sparse_ctx_lens int32 [total_q]: sum over selected b of the visible tokens
  *              of b, min(128, pos - 128*b + 1); 0 when pos < 0.
  */
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride,
-                                 int32_t topk, const int32_t* seq_lens,
-                                 int32_t num_reqs, int32_t query_len,
-                                 int32_t max_seq_len,
+                                 int32_t topk, const mm3_rows* rows,
                                  const int32_t* attention_block_table,
                                  int64_t abt_row_stride, int32_t abt_width,
                                  int32_t pages_per_block,

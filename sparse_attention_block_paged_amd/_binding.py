@@ -39,6 +39,18 @@ class Mm3Error(RuntimeError):
         self.code = code
 
 
+class Rows(ctypes.Structure):
+    _fields_ = [
+        ("seq_lens", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("prefix_lens", ctypes.c_void_p),
+        ("num_reqs", ctypes.c_int32),
+        ("query_len", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+    ]
+
+
 class Problem(ctypes.Structure):
     _fields_ = [
         ("q", ctypes.c_void_p),
@@ -52,11 +64,8 @@ class Problem(ctypes.Structure):
         ("block_table", ctypes.c_void_p),
         ("bt_row_stride", ctypes.c_int64),
         ("bt_width", ctypes.c_int32),
-        ("seq_lens", ctypes.c_void_p),
-        ("num_reqs", ctypes.c_int32),
-        ("query_len", ctypes.c_int32),
-        ("max_seq_len", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
+        ("rows", Rows),
     ]
 
 
@@ -74,17 +83,17 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         PP = ctypes.POINTER(Problem)
+        PR = ctypes.POINTER(Rows)
         L.mm3_index_score.argtypes = [PP, P, I64, I64, I32, P]
         L.mm3_index_score.restype = ctypes.c_int
-        L.mm3_index_topk.argtypes = [P, I64, I64, I32, I32, P, I32, I32, I32, I32, I32, I32,
-                                     P, I64, I64, P]
+        L.mm3_index_topk.argtypes = [P, I64, I64, I32, I32, PR, I32, I32, I32, P, I64, I64, P]
         L.mm3_index_topk.restype = ctypes.c_int
         L.mm3_index_decode_workspace_bytes.argtypes = [PP, I32, I32]
         L.mm3_index_decode_workspace_bytes.restype = SZ
         L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, P]
         L.mm3_index_decode.restype = ctypes.c_int
-        L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, P, I32, I32, I32, P, I64, I32,
-                                                   I32, I32, P, I64, P, P]
+        L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, PR, P, I64, I32, I32, I32, P, I64,
+                                                   P, P]
         L.mm3_build_sparse_block_table.restype = ctypes.c_int
         L.mm3_last_error.argtypes = []
         L.mm3_last_error.restype = ctypes.c_char_p
@@ -120,8 +129,40 @@ def score_width(max_seq_len: int) -> int:
     return cdiv(cdiv(max_seq_len, BLOCK), 16) * 16
 
 
+def _int32_vec(t, n, what):
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.shape[0] != n:
+        raise ValueError(f"{what} must be contiguous int32 [{n}]")
+
+
+def make_rows(seq_lens, query_len, max_seq_len, total_q, cu_seqlens_q=None,
+              prefix_lens=None) -> Rows:
+    """Marshal the row map (uniform, or ragged with cu_seqlens_q and optional
+    prefix_lens; query_len is then the bound on every request's rows)."""
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [reqs]")
+    R = seq_lens.shape[0]
+    if cu_seqlens_q is not None:
+        _int32_vec(cu_seqlens_q, R + 1, "cu_seqlens_q")
+    if prefix_lens is not None:
+        if cu_seqlens_q is None:
+            raise ValueError("prefix_lens needs cu_seqlens_q")
+        _int32_vec(prefix_lens, R, "prefix_lens")
+    for t in (cu_seqlens_q, prefix_lens):
+        if t is not None and t.device != seq_lens.device:
+            raise ValueError("row-map tensors must be on the same device")
+    m = Rows()
+    m.seq_lens = seq_lens.data_ptr()
+    m.cu_seqlens_q = _ptr(cu_seqlens_q)
+    m.prefix_lens = _ptr(prefix_lens)
+    m.num_reqs = R
+    m.query_len = int(query_len)
+    m.total_q = int(total_q)
+    m.max_seq_len = int(max_seq_len)
+    return m
+
+
 def make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
-                 kscales=None) -> Problem:
+                 kscales=None, cu_seqlens_q=None, prefix_lens=None) -> Problem:
     """Marshal tensors into the C problem struct (no copies)."""
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != HEAD_DIM or q.stride(2) != 1:
         raise ValueError("q must be bf16 [tokens, heads, 128] with contiguous D")
@@ -140,8 +181,7 @@ def make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_sca
         kfmt = KFMT_NVFP4
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
         raise ValueError("block_table must be int32 [reqs, width] with unit column stride")
-    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be contiguous int32 [reqs]")
+    rows = make_rows(seq_lens, query_len, max_seq_len, q.shape[0], cu_seqlens_q, prefix_lens)
     devs = {t.device for t in (q, kdata, block_table, seq_lens) + ((kscales,) if kscales is not None else ())}
     if len(devs) != 1:
         raise ValueError("all score inputs must be on the same device")
@@ -157,18 +197,18 @@ def make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_sca
     p.block_table = block_table.data_ptr()
     p.bt_row_stride = block_table.stride(0)
     p.bt_width = block_table.shape[1]
-    p.seq_lens = seq_lens.data_ptr()
-    p.num_reqs = seq_lens.shape[0]
-    p.query_len = int(query_len)
-    p.max_seq_len = int(max_seq_len)
     p.sm_scale = float(sm_scale)
+    p.rows = rows
     return p
 
 
 def mm3_index_score(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
-                    kscales=None, scores=None, stream=None):
-    """Block scores [heads, tokens, width] fp32 (only visible entries written)."""
-    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales)
+                    kscales=None, scores=None, stream=None, cu_seqlens_q=None, prefix_lens=None):
+    """Block scores [heads, tokens, width] fp32 (only visible entries written).
+    Ragged batches: cu_seqlens_q int32 [reqs+1] and optional prefix_lens
+    int32 [reqs] on the device; query_len is then max_query_len."""
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales,
+                     cu_seqlens_q, prefix_lens)
     if scores is None:
         scores = torch.empty((q.shape[1], q.shape[0], score_width(max_seq_len)),
                              dtype=torch.float32, device=q.device)
@@ -180,10 +220,15 @@ def mm3_index_score(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_
 
 
 def mm3_index_topk(scores, seq_lens, query_len, max_seq_len, topk, init_blocks, local_blocks,
-                   out=None, stream=None):
-    """Block ids [heads, tokens, topk] int32, written into out[:, :tokens] in place."""
+                   out=None, stream=None, cu_seqlens_q=None, prefix_lens=None, total_q=None):
+    """Block ids [heads, tokens, topk] int32, written into out[:, :tokens] in place.
+    Ragged batches take tokens from total_q, else from the score tensor's rows."""
     H = scores.shape[0]
-    T = seq_lens.shape[0] * int(query_len)
+    if cu_seqlens_q is None:
+        T = seq_lens.shape[0] * int(query_len)
+    else:
+        T = int(scores.shape[1] if total_q is None else total_q)
+    rows = make_rows(seq_lens, query_len, max_seq_len, T, cu_seqlens_q, prefix_lens)
     if out is None:
         out = torch.empty((H, T, topk), dtype=torch.int32, device=scores.device)
     if scores.dtype != torch.float32 or scores.stride(2) != 1:
@@ -191,11 +236,8 @@ def mm3_index_topk(scores, seq_lens, query_len, max_seq_len, topk, init_blocks, 
     if out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1 or out.shape[2] != topk \
             or out.shape[0] != H or out.shape[1] < T:
         raise ValueError("out must be int32 [heads, >=tokens, topk] with unit column stride")
-    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be contiguous int32")
     _check(lib().mm3_index_topk(scores.data_ptr(), scores.stride(0), scores.stride(1),
-                                scores.shape[2], H, seq_lens.data_ptr(), seq_lens.shape[0],
-                                int(query_len), int(max_seq_len), int(topk), int(init_blocks),
+                                scores.shape[2], H, ctypes.byref(rows), int(topk), int(init_blocks),
                                 int(local_blocks), out.data_ptr(), out.stride(0), out.stride(1),
                                 _stream(scores, stream)))
     return out
@@ -211,9 +253,10 @@ def decode_workspace_bytes(p: Problem, topk: int, with_scores_out: bool) -> int:
 
 def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, topk,
                      init_blocks, local_blocks, kscales=None, out=None, scores_out=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, cu_seqlens_q=None, prefix_lens=None):
     """Scores then top-k in one call; returns out [heads, tokens, topk] int32."""
-    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales)
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales,
+                     cu_seqlens_q, prefix_lens)
     H, T = q.shape[1], q.shape[0]
     if out is None:
         out = torch.empty((H, T, topk), dtype=torch.int32, device=q.device)
@@ -238,7 +281,8 @@ def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm
 
 def mm3_build_sparse_block_table(topk_idx, seq_lens, query_len, max_seq_len,
                                  attention_block_table, pages_per_block, block_page_stride,
-                                 sparse_table=None, sparse_ctx_lens=None, stream=None):
+                                 sparse_table=None, sparse_ctx_lens=None, stream=None,
+                                 cu_seqlens_q=None, prefix_lens=None):
     """(sparse_table [tokens, topk*P], sparse_ctx_lens [tokens]) for one head."""
     if topk_idx.dim() == 3:
         if topk_idx.shape[0] != 1:
@@ -250,15 +294,15 @@ def mm3_build_sparse_block_table(topk_idx, seq_lens, query_len, max_seq_len,
         sparse_table = torch.empty((T, K * P), dtype=torch.int32, device=topk_idx.device)
     if sparse_ctx_lens is None:
         sparse_ctx_lens = torch.empty((T,), dtype=torch.int32, device=topk_idx.device)
-    for t in (topk_idx, attention_block_table, sparse_table, sparse_ctx_lens, seq_lens):
+    for t in (topk_idx, attention_block_table, sparse_table, sparse_ctx_lens):
         if t.dtype != torch.int32 or t.stride(-1) != 1:
             raise ValueError("sparse-table tensors must be int32 with contiguous rows")
+    rows = make_rows(seq_lens, query_len, max_seq_len, T, cu_seqlens_q, prefix_lens)
     _check(lib().mm3_build_sparse_block_table(
-        topk_idx.data_ptr(), topk_idx.stride(0), K, seq_lens.data_ptr(), seq_lens.shape[0],
-        int(query_len), int(max_seq_len), attention_block_table.data_ptr(),
-        attention_block_table.stride(0), attention_block_table.shape[1], P,
-        int(block_page_stride), sparse_table.data_ptr(), sparse_table.stride(0),
-        sparse_ctx_lens.data_ptr(), _stream(topk_idx, stream)))
+        topk_idx.data_ptr(), topk_idx.stride(0), K, ctypes.byref(rows),
+        attention_block_table.data_ptr(), attention_block_table.stride(0),
+        attention_block_table.shape[1], P, int(block_page_stride), sparse_table.data_ptr(),
+        sparse_table.stride(0), sparse_ctx_lens.data_ptr(), _stream(topk_idx, stream)))
     return sparse_table, sparse_ctx_lens
 
 

@@ -1,10 +1,12 @@
 // decode_score.hip -- split-K decode block scorer for gfx950.
 //
 // What it computes (page "vllm.models.minimax_m3.amd.ops.index_topk", module
-// docstring and minimax_m3_index_decode): for each request, its H*Q index
-// query rows (H heads x Q decode positions, <= 16) score every visible
+// docstring and minimax_m3_index_decode): for each request, its H*n index
+// query rows (H heads x n decode positions, <= 16) score every visible
 // 128-token block of the paged, shared index-K cache as the maximum over the
-// block's causally visible tokens of sm_scale * (q . k).
+// block's causally visible tokens of sm_scale * (q . k).  n may differ per
+// request (ragged batches: spec-decode rows, or the decode part of a mixed
+// batch).
 //
 // Design.  Decode is a bandwidth-bound GEMV: every key (256 B bf16, 72 B
 // NVFP4) is read once and serves all H*Q rows of its request.  One wavefront
@@ -26,6 +28,7 @@
 #include "mm3_device.h"
 #include "mm3_fp4.h"
 #include "mm3_launch.h"
+#include "mm3_rows.h"
 
 namespace mm3 {
 
@@ -56,6 +59,22 @@ struct HalfBuf<1> {
   u32x2 scl;  // the 8 scale bytes of token l of the half (lane l)
 };
 
+// A decode request's first-row position and row count (<= 16) in one word.
+__device__ __forceinline__ int pack_req(int p0, int n) { return p0 * 32 + n; }
+__device__ __forceinline__ int packed_p0(int v) { return v >> 5; }  // arithmetic: floor
+__device__ __forceinline__ int packed_n(int v) { return v & 31; }
+
+// The block a wave works on: request r, logical block b, the request's rows
+// (pack_req of the first one's position and their count; the first row) and
+// the page the block table maps b to (all wave-uniform).
+struct Cur {
+  int r;
+  int b;
+  int pk;
+  int row0;
+  int64_t page;
+};
+
 struct QRows {
   bf16x8 qb[4];
   int pos;   // position of this lane's row (MFMA column n), -1 if none
@@ -74,15 +93,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
-// Issue the query loads of request r: column n = row j*H + h of the request.
-// Lanes without a row (n >= H*Q) and calls with live == false get zeros.
+// Issue the query loads of c's request: column n = row j*H + h of the
+// request.  Lanes without a row (n >= H*rows) and calls with live == false
+// get zeros.
 template <int KFMT>
-__device__ __forceinline__ QRaw issue_q(const ScoreArgs& a, int r, int n, int g, bool live) {
-  const int H = a.heads, Q = a.qlen;
+__device__ __forceinline__ QRaw issue_q(const ScoreArgs& a, const Cur& c, int n, int g, bool live) {
+  const int H = a.heads;
   const int j = n / H, h = n - (n / H) * H;
-  const uint16_t* base = a.q + (int64_t)r * Q * a.q_tok;
+  const uint16_t* base = a.q + (int64_t)c.row0 * a.q_tok;
   const __amdgpu_buffer_rsrc_t rs = rsrc(base, live ? 0x7FFFFFF0 : 0);
-  const int row = n < H * Q ? (int)(((int64_t)j * a.q_tok + (int64_t)h * a.q_head) * 2) : 0x7FFFFFF0;
+  const int row = n < H * packed_n(c.pk) ? (int)(((int64_t)j * a.q_tok + (int64_t)h * a.q_head) * 2) : 0x7FFFFFF0;
   QRaw q;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
@@ -103,15 +123,15 @@ __device__ __forceinline__ uint32_t opaque_mov(uint32_t v) {
   return r;
 }
 
-// Finish the query operands of request r (row bookkeeping; NVFP4 element
+// Finish the query operands of c's request (row bookkeeping; NVFP4 element
 // order {0,2,4,6,1,3,5,7} within each 8-element step to match the keys).
 template <int KFMT>
-__device__ __forceinline__ void set_q(QRows& q, const QRaw& raw, const ScoreArgs& a, int r, int seq, int n) {
-  const int H = a.heads, Q = a.qlen;
+__device__ __forceinline__ void set_q(QRows& q, const QRaw& raw, const ScoreArgs& a, const Cur& c, int n) {
+  const int H = a.heads;
   const int j = n / H;
   q.h = n - j * H;
-  q.t = r * Q + j;
-  q.pos = n < H * Q ? seq - Q + j : -1;
+  q.t = c.row0 + j;
+  q.pos = n < H * packed_n(c.pk) ? packed_p0(c.pk) + j : -1;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     const u32x4 v = raw.v[kc];
@@ -235,15 +255,6 @@ __device__ __forceinline__ void compute_half(const HalfBuf<KFMT>& buf, const QRo
   }
 }
 
-// The block a wave works on: request r, logical block b, the request's
-// length and the page the block table maps b to (all wave-uniform).
-struct Cur {
-  int r;
-  int b;
-  int seq;
-  int64_t page;
-};
-
 __device__ __forceinline__ int64_t page_of(const ScoreArgs& a, int r, int b) {
   const int32_t __attribute__((address_space(4)))* bt =
       (const int32_t __attribute__((address_space(4)))*)a.bt;
@@ -310,14 +321,14 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut,
                                            float* stv, int32_t* sto) {
   constexpr int DB = kRingBlocks<KFMT>;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int HQ = a.heads * a.qlen;
+  const int HQ = a.heads * a.rows.qlen;  // stage columns: the most rows a request has
   const int stage_blocks = kStage / HQ;
   RingBlock<KFMT> ring[DB];
   if (!walk.first(ring[0].c)) return;
   QRows q;
   {
-    const QRaw raw = issue_q<KFMT>(a, ring[0].c.r, n, g, true);
-    set_q<KFMT>(q, raw, a, ring[0].c.r, ring[0].c.seq, n);
+    const QRaw raw = issue_q<KFMT>(a, ring[0].c, n, g, true);
+    set_q<KFMT>(q, raw, a, ring[0].c, n);
   }
   ring[0].live = true;
   ring[0].new_req = false;
@@ -332,7 +343,7 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut,
     rb.live = more && walk.next(rb.c);
     more = rb.live;
     rb.new_req = rb.live && rb.c.r != last.r;
-    rb.qraw = issue_q<KFMT>(a, rb.c.r, n, g, rb.new_req);
+    rb.qraw = issue_q<KFMT>(a, rb.c, n, g, rb.new_req);
     issue_half<KFMT>(rb.h0, a, rb.c.page, 0, n, g, rb.live);
     issue_half<KFMT>(rb.h1, a, rb.c.page, 1, n, g, rb.live);
     if (rb.live) last = rb.c;
@@ -345,19 +356,19 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut,
       RingBlock<KFMT>& rb = ring[j];
       if (!rb.live) goto done;
       const Cur cur = rb.c;
-      if (rb.new_req) set_q<KFMT>(q, rb.qraw, a, cur.r, cur.seq, n);
+      if (rb.new_req) set_q<KFMT>(q, rb.qraw, a, cur, n);
       // the block that takes this slot
       Cur nxt = last;
       const bool has_next = more && walk.next(nxt);
       more = has_next;
       const bool new_req = has_next && nxt.r != last.r;
       __builtin_amdgcn_sched_barrier(0);
-      const bool full = kBlock * cur.b + (kBlock - 1) <= cur.seq - a.qlen;
+      const bool full = kBlock * cur.b + (kBlock - 1) <= packed_p0(cur.pk);  // the first row sees all of it
       const int lim = q.pos - kBlock * cur.b;
       float m = -INFINITY;
       compute_half<KFMT>(rb.h0, q, lut, tb, 0, full, lim, n, g, m);
       __builtin_amdgcn_sched_barrier(0);
-      rb.qraw = issue_q<KFMT>(a, nxt.r, n, g, new_req);
+      rb.qraw = issue_q<KFMT>(a, nxt, n, g, new_req);
       issue_half<KFMT>(rb.h0, a, nxt.page, 0, n, g, has_next);
       __builtin_amdgcn_sched_barrier(0);
       compute_half<KFMT>(rb.h1, q, lut, tb, 1, full, lim, n, g, m);
@@ -406,7 +417,8 @@ done:
 struct SharedWalk {
   const ScoreArgs* a;
   const int32_t* pre;  // LDS: pre[r] = blocks of requests < r
-  const int32_t* sl;   // LDS: seq_lens
+  const int32_t* sl;   // LDS: pack_req(p0, rows) per request
+  const int32_t* r0;   // LDS: first row per request
   uint32_t* counter;   // LDS: next block of the slice, counted from lo
   int64_t lo, hi;      // the workgroup's slice of the flattened block list
   int64_t gb;          // the block just taken
@@ -421,7 +433,8 @@ struct SharedWalk {
   __device__ __forceinline__ void fill(Cur& c) {
     req_lo = __builtin_amdgcn_readfirstlane(pre[c.r]);
     req_hi = __builtin_amdgcn_readfirstlane(pre[c.r + 1]);
-    c.seq = __builtin_amdgcn_readfirstlane(sl[c.r]);
+    c.pk = __builtin_amdgcn_readfirstlane(sl[c.r]);
+    c.row0 = __builtin_amdgcn_readfirstlane(r0[c.r]);
     c.b = (int)(gb - req_lo);
     // finish the LDS reads before the scalar page load, so that later waits
     // on LDS never also wait on that load
@@ -430,7 +443,7 @@ struct SharedWalk {
   }
   __device__ __forceinline__ bool first(Cur& c) {
     if (!take()) return false;
-    int l = 0, u = a->num_reqs;  // last r with pre[r] <= gb
+    int l = 0, u = a->rows.num_reqs;  // last r with pre[r] <= gb
     while (u - l > 1) {
       const int mid = (l + u) >> 1;
       if (pre[mid] <= gb) l = mid; else u = mid;
@@ -471,16 +484,20 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs
   __shared__ float stage_v[W][kStage];
   __shared__ int32_t stage_o[W][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[W][KFMT == 0 ? kTransposeBytes : 16];
-  const int R = a.num_reqs;
-  int32_t* pre = smem;         // [R + 1]
-  int32_t* sl = smem + R + 1;  // [R]
+  const int R = a.rows.num_reqs;
+  int32_t* pre = smem;              // [R + 1]
+  int32_t* sl = smem + R + 1;       // [R]
+  int32_t* r0s = smem + 2 * R + 1;  // [R]
   const int per = (R + NT - 1) / NT;
   const int r0 = min(R, (int)threadIdx.x * per), r1 = min(R, r0 + per);
   int sum = 0;
   for (int r = r0; r < r1; ++r) {
-    const int s = a.seq_lens[r];
-    sl[r] = s;
-    sum += s > 0 ? (s - 1) / kBlock + 1 : 0;
+    const ReqRows q = req_rows(a.rows, r);
+    // requests this launch does not take count as no rows
+    const int v = routed(a.route, a.heads, q.n) ? pack_req(q.p0, q.n) : pack_req(0, 0);
+    sl[r] = v;
+    r0s[r] = q.row0;
+    sum += req_blocks(packed_p0(v), packed_n(v));
   }
   if constexpr (KFMT == 1) {
     if (threadIdx.x < 256) fill_lut(lut);
@@ -507,15 +524,15 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs
   }
   for (int r = r0; r < r1; ++r) {
     pre[r] = base;
-    const int s = sl[r];
-    base += s > 0 ? (s - 1) / kBlock + 1 : 0;
+    const int v = sl[r];
+    base += req_blocks(packed_p0(v), packed_n(v));
   }
   if (threadIdx.x == NT - 1) pre[R] = total_blocks;
   __syncthreads();
   const int64_t total = total_blocks;
   const int64_t lo = total * blockIdx.x / gridDim.x;
   const int64_t hi = total * (blockIdx.x + 1) / gridDim.x;
-  SharedWalk walk{&a, pre, sl, &next_blk, lo, hi, 0, 0, 0};
+  SharedWalk walk{&a, pre, sl, r0s, &next_blk, lo, hi, 0, 0, 0};
   score_wave<KFMT, true>(a, lut, tbuf[wave], walk, stage_v[wave], stage_o[wave]);
 }
 
@@ -526,12 +543,14 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs
 
 struct ChunkWalk {
   const ScoreArgs* a;
-  int r, seq, b, b_end;
-  __device__ __forceinline__ int count() const { return (b_end - b + 3) / 4; }  // valid after first()
+  int r;
+  ReqRows rr;
+  int b, b_end;
   __device__ __forceinline__ bool first(Cur& c) {
     if (b >= b_end) return false;
     c.r = r;
-    c.seq = seq;
+    c.pk = pack_req(rr.p0, rr.n);
+    c.row0 = rr.row0;
     c.b = b;
     c.page = page_of(*a, r, b);
     return true;
@@ -550,9 +569,9 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
   __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[4][KFMT == 0 ? kTransposeBytes : 16];
   const int r = blockIdx.y;
-  const int seq = a.seq_lens[r];
-  if (seq <= 0) return;
-  const int nb = (seq - 1) / kBlock + 1;
+  const ReqRows rr = req_rows(a.rows, r);
+  if (!routed(a.route, a.heads, rr.n)) return;
+  const int nb = req_blocks(rr.p0, rr.n);
   const int b_begin = blockIdx.x * a.blocks_per_wg;
   if (b_begin >= nb) return;
   if constexpr (KFMT == 1) {
@@ -560,7 +579,7 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
     __syncthreads();
   }
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  ChunkWalk walk{&a, r, seq, b_begin + wave, min(nb, b_begin + a.blocks_per_wg)};
+  ChunkWalk walk{&a, r, rr, b_begin + wave, min(nb, b_begin + a.blocks_per_wg)};
   score_wave<KFMT, false>(a, lut, tbuf[wave], walk, nullptr, nullptr);
 }
 
@@ -583,13 +602,13 @@ int device_cus() {
 
 template <int KFMT>
 static hipError_t launch_decode(const ScoreArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)(2 * a.num_reqs + 1) * sizeof(int32_t);
-  if (a.num_reqs <= kCuMaxReqs && a.s_bytes > 0) {
+  const size_t lds = (size_t)(3 * a.rows.num_reqs + 1) * sizeof(int32_t);
+  if (a.rows.num_reqs <= kCuMaxReqs && a.s_bytes > 0) {
     // one workgroup per CU: its LDS and registers leave room for no second
     hipLaunchKernelGGL(decode_score_cu<KFMT>, dim3(device_cus()), dim3(64 * kCuWaves<KFMT>), lds, s, a);
   } else {
     const int chunks = (a.nb_max + a.blocks_per_wg - 1) / a.blocks_per_wg;
-    hipLaunchKernelGGL(decode_score_chunked<KFMT>, dim3(chunks, a.num_reqs, 1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_score_chunked<KFMT>, dim3(chunks, a.rows.num_reqs, 1), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

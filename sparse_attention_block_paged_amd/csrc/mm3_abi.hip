@@ -41,27 +41,50 @@ bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The row map every entry point takes (page "ops.index_topk":
+// minimax_m3_index_decode for uniform batches, minimax_m3_index_score and
+// minimax_m3_index_topk for cu_seqlens_q / prefix_lens; page
+// "indexer_context_parallel", check_context_score_inputs: tokens ==
+// requests * query_len).  heads is 0 when the caller has no heads.
+int check_rows(const mm3_rows* m, int32_t heads) {
+  if (!m) return fail(MM3_EINVAL, "rows is NULL");
+  if (m->query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1, got %d", m->query_len);
+  if (m->num_reqs < 0) return fail(MM3_EINVAL, "num_reqs must be >= 0, got %d", m->num_reqs);
+  if (m->total_q < 0) return fail(MM3_EINVAL, "total_q must be >= 0, got %d", m->total_q);
+  if (m->max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
+  if (!m->seq_lens) return fail(MM3_EINVAL, "seq_lens must be non-NULL");
+  if (!aligned(m->seq_lens, 4) || !aligned(m->cu_seqlens_q, 4) || !aligned(m->prefix_lens, 4))
+    return fail(MM3_EINVAL, "seq_lens, cu_seqlens_q and prefix_lens must be 4-byte aligned");
+  if ((int64_t)heads * m->query_len > INT32_MAX)
+    return fail(MM3_EINVAL, "heads * query_len must be below 2^31");
+  if (!m->cu_seqlens_q) {
+    if (m->prefix_lens) return fail(MM3_EINVAL, "prefix_lens needs cu_seqlens_q");
+    if ((int64_t)m->num_reqs * m->query_len != m->total_q)
+      return fail(MM3_EINVAL, "total_q (%d) must equal num_reqs * query_len (%lld) without cu_seqlens_q",
+                  m->total_q, (long long)m->num_reqs * m->query_len);
+  }
+  const int64_t nb = cdiv64(m->max_seq_len, MM3_BLOCK);
+  if (nb > MM3_MAX_BLOCKS)
+    return fail(MM3_EINVAL, "cdiv(max_seq_len,128) = %lld must be below 65535", (long long)nb);
+  return MM3_OK;
+}
+
 // Rules every scorer entry point shares (page "indexer_context_parallel",
 // check_context_score_inputs and indexer_context_scores; page
 // "ops.index_topk", minimax_m3_index_decode).
 int check_problem(const mm3_problem* p) {
   if (!p) return fail(MM3_EINVAL, "problem is NULL");
   if (p->heads < 1) return fail(MM3_EINVAL, "heads must be >= 1, got %d", p->heads);
-  if (p->query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1, got %d", p->query_len);
-  if (p->num_reqs < 0) return fail(MM3_EINVAL, "num_reqs must be >= 0, got %d", p->num_reqs);
-  if (p->max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
-  if ((int64_t)p->num_reqs * p->query_len > INT32_MAX || (int64_t)p->heads * p->query_len > INT32_MAX)
-    return fail(MM3_EINVAL, "num_reqs * query_len and heads * query_len must be below 2^31");
-  const int64_t nb = cdiv64(p->max_seq_len, MM3_BLOCK);
-  if (nb > MM3_MAX_BLOCKS)
-    return fail(MM3_EINVAL, "cdiv(max_seq_len,128) = %lld must be below 65535", (long long)nb);
+  int rc = check_rows(&p->rows, p->heads);
+  if (rc) return rc;
+  const int64_t nb = cdiv64(p->rows.max_seq_len, MM3_BLOCK);
   if (!(isfinite(p->sm_scale) && p->sm_scale > 0.0f))
     return fail(MM3_EINVAL, "sm_scale must be finite and > 0");
   if (p->kfmt != MM3_KFMT_BF16 && p->kfmt != MM3_KFMT_NVFP4)
     return fail(MM3_EINVAL, "unknown index-K format %d", p->kfmt);
   if (p->num_pages < 1) return fail(MM3_EINVAL, "index cache must hold >= 1 page");
-  if (!p->q || !p->kdata || !p->block_table || !p->seq_lens)
-    return fail(MM3_EINVAL, "q, kdata, block_table and seq_lens must be non-NULL");
+  if (!p->q || !p->kdata || !p->block_table)
+    return fail(MM3_EINVAL, "q, kdata and block_table must be non-NULL");
   if (p->kfmt == MM3_KFMT_NVFP4 && !p->kscales)
     return fail(MM3_EINVAL, "NVFP4 index cache needs kscales");
   if (!aligned(p->q, 16) || !aligned(p->kdata, 16) || (p->kscales && !aligned(p->kscales, 2)))
@@ -73,14 +96,14 @@ int check_problem(const mm3_problem* p) {
   if (p->bt_width < nb)
     return fail(MM3_EINVAL, "block table width %d narrower than cdiv(max_seq_len,128) = %lld",
                 p->bt_width, (long long)nb);
-  if (p->num_reqs > 1 && p->bt_row_stride < p->bt_width)
+  if (p->rows.num_reqs > 1 && p->bt_row_stride < p->bt_width)
     return fail(MM3_EINVAL, "block table row stride must be >= its width");
   return MM3_OK;
 }
 
 int check_scores(const mm3_problem* p, const float* s, int64_t sh, int64_t sr, int32_t sw) {
-  const int64_t T = (int64_t)p->num_reqs * p->query_len;
-  const int64_t nb = cdiv64(p->max_seq_len, MM3_BLOCK);
+  const int64_t T = p->rows.total_q;
+  const int64_t nb = cdiv64(p->rows.max_seq_len, MM3_BLOCK);
   if (!s) return fail(MM3_EINVAL, "scores must be non-NULL");
   if (!aligned(s, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
   if (sw < nb) return fail(MM3_EINVAL, "score width %d < cdiv(max_seq_len,128) = %lld", sw, (long long)nb);
@@ -107,6 +130,17 @@ int check_out(int32_t* out, int64_t oh, int64_t orow, int32_t heads, int64_t T, 
   return MM3_OK;
 }
 
+Rows rows_of(const mm3_rows* m) {
+  Rows r{};
+  r.seq_lens = m->seq_lens;
+  r.cu = m->cu_seqlens_q;
+  r.prefix = m->cu_seqlens_q ? m->prefix_lens : nullptr;
+  r.num_reqs = m->num_reqs;
+  r.qlen = m->query_len;
+  r.tokens = m->total_q;
+  return r;
+}
+
 ScoreArgs score_args(const mm3_problem* p, float* s, int64_t sh, int64_t sr) {
   ScoreArgs a{};
   a.q = static_cast<const uint16_t*>(p->q);
@@ -116,59 +150,69 @@ ScoreArgs score_args(const mm3_problem* p, float* s, int64_t sh, int64_t sr) {
   a.kscales = p->kscales;
   a.bt = p->block_table;
   a.bt_stride = p->bt_row_stride;
-  a.seq_lens = p->seq_lens;
+  a.rows = rows_of(&p->rows);
   a.scores = s;
   a.s_head = sh;
   a.s_row = sr;
   a.heads = p->heads;
-  a.qlen = p->query_len;
-  a.num_reqs = p->num_reqs;
-  a.nb_max = (int32_t)cdiv64(p->max_seq_len, MM3_BLOCK);
+  a.route = kRouteAll;
+  a.nb_max = (int32_t)cdiv64(p->rows.max_seq_len, MM3_BLOCK);
   a.sm_scale = p->sm_scale;
-  // Decode: each wave scores a few pages; aim for enough workgroups to
-  // cover the chip several times at the capture-stable size.
-  const int64_t total = (int64_t)p->num_reqs * a.nb_max;
+  // Decode fallback grid: each wave scores a few pages; aim for enough
+  // workgroups to cover the chip several times at the capture-stable size.
+  const int64_t total = (int64_t)p->rows.num_reqs * a.nb_max;
   int bpw = 4;  // blocks per workgroup (4 waves)
   while (bpw < 32 && total / bpw > 8192) bpw *= 2;
   a.blocks_per_wg = bpw;
-  const int64_t T = (int64_t)p->num_reqs * p->query_len;
+  const int64_t T = p->rows.total_q;
   const int64_t extent = T == 0 ? 0 : ((int64_t)(p->heads - 1) * sh + (T - 1) * sr + a.nb_max) * 4;
   a.s_bytes = extent <= 0x7FFFFFC0 ? (int32_t)extent : 0;
   return a;
 }
 
-bool is_decode_shape(const mm3_problem* p) {
-  return (int64_t)p->heads * p->query_len <= kDecodeRows;
-}
-
+// Launch policy.  A request with heads * n_r <= 16 rows goes to the decode
+// scorer (one MFMA tile of query rows, bandwidth-bound), a larger one to the
+// MFMA prefill scorer.  Uniform batches take one of them for every request.
+// Ragged batches may hold both kinds, so both launch, each taking only its
+// own requests (decided on the device from cu_seqlens_q); the decode one
+// sizes its query tile for the largest row count it can take.
 int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStream_t st) {
-  const ScoreArgs a = score_args(p, s, sh, sr);
-  hipError_t e;
-  if (is_decode_shape(p))
-    e = p->kfmt == MM3_KFMT_BF16 ? launch_decode_score_bf16(a, st) : launch_decode_score_nvfp4(a, st);
-  else
-    e = p->kfmt == MM3_KFMT_BF16 ? launch_prefill_score_bf16(a, st) : launch_prefill_score_nvfp4(a, st);
+  ScoreArgs a = score_args(p, s, sh, sr);
+  const bool bf16 = p->kfmt == MM3_KFMT_BF16;
+  const int64_t H = p->heads, Q = p->rows.query_len;
+  bool decode, prefill;
+  ScoreArgs d = a, f = a;
+  if (!p->rows.cu_seqlens_q) {
+    decode = H * Q <= kDecodeRows;
+    prefill = !decode;
+  } else {
+    decode = H <= kDecodeRows;
+    prefill = H * Q > kDecodeRows;
+    d.route = kRouteDecode;
+    d.rows.qlen = (int32_t)(Q < kDecodeRows / H ? Q : kDecodeRows / H);
+    f.route = kRoutePrefill;
+  }
+  hipError_t e = hipSuccess;
+  if (decode) e = bf16 ? launch_decode_score_bf16(d, st) : launch_decode_score_nvfp4(d, st);
+  if (e == hipSuccess && prefill) e = bf16 ? launch_prefill_score_bf16(f, st) : launch_prefill_score_nvfp4(f, st);
   return e == hipSuccess ? MM3_OK : hip_fail(e, "scorer launch");
 }
 
-TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t heads, const int32_t* seq,
-                   int32_t R, int32_t Q, int32_t max_seq_len, int32_t topk, int32_t I, int32_t L,
-                   int32_t* out, int64_t oh, int64_t orow) {
+TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t heads, const mm3_rows* rows,
+                   int32_t topk, int32_t I, int32_t L, int32_t* out, int64_t oh, int64_t orow) {
   TopkArgs a{};
   a.scores = s;
   a.s_head = sh;
   a.s_row = sr;
-  a.seq_lens = seq;
+  a.rows = rows_of(rows);
   a.out = out;
   a.o_head = oh;
   a.o_row = orow;
   a.heads = heads;
-  a.qlen = Q;
-  a.num_reqs = R;
   a.topk = topk;
   a.init_blocks = I;
   a.local_blocks = L;
-  a.nb_max = (int32_t)cdiv64(max_seq_len, MM3_BLOCK);
+  a.nb_max = (int32_t)cdiv64(rows->max_seq_len, MM3_BLOCK);
   return a;
 }
 
@@ -187,25 +231,21 @@ int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_scores(p, scores, s_head_stride, s_row_stride, s_width))) return rc;
-  if ((int64_t)p->num_reqs * p->query_len == 0 || p->max_seq_len == 0) return ok();
+  if (p->rows.total_q == 0 || p->rows.max_seq_len == 0) return ok();
   if ((rc = launch_scores(p, scores, s_head_stride, s_row_stride, (hipStream_t)stream))) return rc;
   return ok();
 }
 
 int mm3_index_topk(const float* scores, int64_t s_head_stride, int64_t s_row_stride,
-                   int32_t s_width, int32_t heads, const int32_t* seq_lens, int32_t num_reqs,
-                   int32_t query_len, int32_t max_seq_len, int32_t topk, int32_t init_blocks,
-                   int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                   int32_t s_width, int32_t heads, const mm3_rows* rows, int32_t topk,
+                   int32_t init_blocks, int32_t local_blocks, int32_t* out, int64_t o_head_stride,
                    int64_t o_row_stride, void* stream) {
   if (heads < 1) return fail(MM3_EINVAL, "heads must be >= 1");
-  if (query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1");
-  if (num_reqs < 0 || max_seq_len < 0) return fail(MM3_EINVAL, "num_reqs and max_seq_len must be >= 0");
-  const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
-  if (nb > MM3_MAX_BLOCKS) return fail(MM3_EINVAL, "cdiv(max_seq_len,128) must be below 65535");
-  int rc = check_select(topk, init_blocks, local_blocks);
+  int rc = check_rows(rows, 0);
   if (rc) return rc;
-  const int64_t T = (int64_t)num_reqs * query_len;
-  if (!seq_lens) return fail(MM3_EINVAL, "seq_lens must be non-NULL");
+  const int64_t nb = cdiv64(rows->max_seq_len, MM3_BLOCK);
+  if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
+  const int64_t T = rows->total_q;
   if (!scores) return fail(MM3_EINVAL, "scores must be non-NULL");
   if (!aligned(scores, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
   if (s_width < nb) return fail(MM3_EINVAL, "score width < cdiv(max_seq_len,128)");
@@ -215,8 +255,8 @@ int mm3_index_topk(const float* scores, int64_t s_head_stride, int64_t s_row_str
     return fail(MM3_EINVAL, "score head stride must be >= tokens * row stride");
   if ((rc = check_out(out, o_head_stride, o_row_stride, heads, T, topk))) return rc;
   if (T == 0) return ok();
-  TopkArgs a = topk_args(scores, s_head_stride, s_row_stride, heads, seq_lens, num_reqs, query_len,
-                         max_seq_len, topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride);
+  TopkArgs a = topk_args(scores, s_head_stride, s_row_stride, heads, rows, topk, init_blocks,
+                         local_blocks, out, o_head_stride, o_row_stride);
   hipError_t e = launch_topk(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
@@ -227,8 +267,8 @@ size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk, int3
   if (check_select(topk, 0, 0)) return 0;
   g_err.clear();
   if (with_scores_out) return 0;
-  const int64_t T = (int64_t)p->num_reqs * p->query_len;
-  const int64_t width = cdiv64(cdiv64(p->max_seq_len, MM3_BLOCK), 16) * 16;
+  const int64_t T = p->rows.total_q;
+  const int64_t width = cdiv64(cdiv64(p->rows.max_seq_len, MM3_BLOCK), 16) * 16;
   return round256((size_t)(p->heads * T * width) * sizeof(float));
 }
 
@@ -240,7 +280,7 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
-  const int64_t T = (int64_t)p->num_reqs * p->query_len;
+  const int64_t T = p->rows.total_q;
   if ((rc = check_out(out, o_head_stride, o_row_stride, p->heads, T, topk))) return rc;
   float* s = scores_out;
   int64_t sh = s_head_stride, sr = s_row_stride;
@@ -252,44 +292,42 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
       return fail(MM3_EWORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes (got %zu)",
                   need, workspace_bytes);
-    sw = (int32_t)(cdiv64(cdiv64(p->max_seq_len, MM3_BLOCK), 16) * 16);
+    sw = (int32_t)(cdiv64(cdiv64(p->rows.max_seq_len, MM3_BLOCK), 16) * 16);
     sr = sw;
     sh = T * sr;
     s = static_cast<float*>(workspace);
   }
   if (T == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
-  if (p->max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
-  TopkArgs a = topk_args(s, sh, sr, p->heads, p->seq_lens, p->num_reqs, p->query_len, p->max_seq_len,
-                         topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride);
+  if (p->rows.max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
+  TopkArgs a = topk_args(s, sh, sr, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
+                         o_head_stride, o_row_stride);
   hipError_t e = launch_topk(a, st);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
 }
 
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, int32_t topk,
-                                 const int32_t* seq_lens, int32_t num_reqs, int32_t query_len,
-                                 int32_t max_seq_len, const int32_t* attention_block_table,
+                                 const mm3_rows* rows, const int32_t* attention_block_table,
                                  int64_t abt_row_stride, int32_t abt_width,
                                  int32_t pages_per_block, int32_t block_page_stride,
                                  int32_t* sparse_table, int64_t st_row_stride,
                                  int32_t* sparse_ctx_lens, void* stream) {
-  if (!topk_idx || !seq_lens || !attention_block_table || !sparse_table || !sparse_ctx_lens)
+  if (!topk_idx || !attention_block_table || !sparse_table || !sparse_ctx_lens)
     return fail(MM3_EINVAL, "sparse-table arguments must be provided together (non-NULL)");
   if (topk < 1 || topk > MM3_MAX_TOPK) return fail(MM3_EINVAL, "topk must be in [1, 1024]");
-  if (query_len < 1 || num_reqs < 0 || max_seq_len < 0)
-    return fail(MM3_EINVAL, "query_len >= 1, num_reqs >= 0, max_seq_len >= 0 required");
-  const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
-  if (nb > MM3_MAX_BLOCKS) return fail(MM3_EINVAL, "cdiv(max_seq_len,128) must be below 65535");
+  int rc = check_rows(rows, 0);
+  if (rc) return rc;
+  const int64_t nb = cdiv64(rows->max_seq_len, MM3_BLOCK);
   if (pages_per_block < 1) return fail(MM3_EINVAL, "pages_per_block must be >= 1");
   if (block_page_stride != pages_per_block && block_page_stride != 2 * pages_per_block)
     return fail(MM3_EINVAL, "block_page_stride must be P or 2P (P=%d), got %d", pages_per_block,
                 block_page_stride);
   if ((int64_t)abt_width < nb * block_page_stride)
     return fail(MM3_EINVAL, "attention block table narrower than cdiv(max_seq_len,128)*stride");
-  if (num_reqs > 1 && abt_row_stride < abt_width)
+  if (rows->num_reqs > 1 && abt_row_stride < abt_width)
     return fail(MM3_EINVAL, "attention block table row stride must be >= its width");
-  const int64_t T = (int64_t)num_reqs * query_len;
+  const int64_t T = rows->total_q;
   if (T > 1 && o_row_stride < topk) return fail(MM3_EINVAL, "topk row stride must be >= topk");
   if (T > 1 && st_row_stride < (int64_t)topk * pages_per_block)
     return fail(MM3_EINVAL, "sparse table row stride must be >= topk * pages_per_block");
@@ -300,15 +338,13 @@ int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, 
   SparseTableArgs a{};
   a.topk_idx = topk_idx;
   a.o_row = o_row_stride;
-  a.seq_lens = seq_lens;
+  a.rows = rows_of(rows);
   a.abt = attention_block_table;
   a.abt_row = abt_row_stride;
   a.sparse = sparse_table;
   a.st_row = st_row_stride;
   a.ctx_lens = sparse_ctx_lens;
   a.topk = topk;
-  a.qlen = query_len;
-  a.num_reqs = num_reqs;
   a.pages_per_block = pages_per_block;
   a.block_page_stride = block_page_stride;
   hipError_t e = launch_sparse_table(a, (hipStream_t)stream);

@@ -7,6 +7,26 @@
 
 namespace mm3 {
 
+// The batch's rows.  Uniform (cu == nullptr): request r owns rows
+// [r*qlen, (r+1)*qlen) and its row j sits at seq_lens[r] - qlen + j.
+// Ragged: rows [cu[r], cu[r+1]); row j at prefix[r] + j, or at
+// seq_lens[r] - n_r + j without prefix.  qlen bounds every n_r.
+struct Rows {
+  const int32_t* seq_lens;
+  const int32_t* cu;
+  const int32_t* prefix;
+  int32_t num_reqs;
+  int32_t qlen;
+  int32_t tokens;
+};
+
+// Which requests a scorer launch takes (a ragged batch may need both).
+enum Route : int32_t {
+  kRouteAll = 0,      // every request
+  kRouteDecode = 1,   // requests with heads * n_r <= kDecodeRows
+  kRoutePrefill = 2,  // requests with heads * n_r > kDecodeRows
+};
+
 // Everything a scorer reads.  Strides in elements.
 struct ScoreArgs {
   const uint16_t* q;        // bf16 bits [T, H, 128]
@@ -16,13 +36,12 @@ struct ScoreArgs {
   const uint8_t* kscales;   // nvfp4 e4m3 scales [P,128,8]
   const int32_t* bt;
   int64_t bt_stride;
-  const int32_t* seq_lens;
+  Rows rows;                // qlen: rows per request this launch handles at most
   float* scores;            // [H, T, >=nb] fp32
   int64_t s_head;
   int64_t s_row;
   int32_t heads;
-  int32_t qlen;
-  int32_t num_reqs;
+  int32_t route;            // Route
   int32_t nb_max;           // cdiv(max_seq_len, 128)
   int32_t blocks_per_wg;    // decode: blocks one workgroup covers
   int32_t s_bytes;          // bytes from scores to one past its last element
@@ -34,13 +53,11 @@ struct TopkArgs {
   const float* scores;
   int64_t s_head;
   int64_t s_row;
-  const int32_t* seq_lens;
+  Rows rows;
   int32_t* out;
   int64_t o_head;
   int64_t o_row;
   int32_t heads;
-  int32_t qlen;
-  int32_t num_reqs;
   int32_t topk;
   int32_t init_blocks;
   int32_t local_blocks;
@@ -50,15 +67,13 @@ struct TopkArgs {
 struct SparseTableArgs {
   const int32_t* topk_idx;
   int64_t o_row;
-  const int32_t* seq_lens;
+  Rows rows;
   const int32_t* abt;
   int64_t abt_row;
   int32_t* sparse;
   int64_t st_row;
   int32_t* ctx_lens;
   int32_t topk;
-  int32_t qlen;
-  int32_t num_reqs;
   int32_t pages_per_block;
   int32_t block_page_stride;
 };

@@ -3,7 +3,8 @@
 // What it computes (page "vllm.models.minimax_m3.amd.ops.index_topk",
 // minimax_m3_index_score: per query token and head, the largest scaled
 // dot product over the causally visible keys of each 128-token index-K
-// block; causal within the chunk).
+// block; causal within the chunk; chunks of different lengths and prefixes
+// in one ragged batch).
 //
 // Design.  With many query rows per request the score is a dense product
 // [rows x 128] . [128 x keys] followed by a max over each 128-key block, so it
@@ -35,6 +36,7 @@
 #include "mm3_device.h"
 #include "mm3_fp4.h"
 #include "mm3_launch.h"
+#include "mm3_rows.h"
 
 namespace mm3 {
 
@@ -82,11 +84,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Blocks that the last row of row tile x can see (0 if none): the tile's
-// step count.  Rows are ordered by position, so the last row bounds them all.
-__device__ __forceinline__ int tile_blocks(int seq, int x, int H, int Q, int HQ) {
+// Blocks that the last row of row tile x of a request (n positions from p0,
+// H heads each) can see: the tile's step count, 0 for a tile past the
+// request's rows.  Rows are ordered by position, so the last row bounds them.
+__device__ __forceinline__ int tile_blocks(int p0, int n, int x, int H) {
+  const int HQ = H * n;
+  if (x * kPrefillRows >= HQ) return 0;
   const int rl = min(HQ, (x + 1) * kPrefillRows) - 1;
-  const int pl = seq - Q + rl / H;
+  const int pl = p0 + rl / H;
   return pl < 0 ? 0 : pl / kBlock + 1;
 }
 
@@ -120,9 +125,11 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// Position in the list of (unit, block) steps.
+// Position in the list of (unit, block) steps: unit u = row tile x of
+// request r (rows row0.., n of them, positions p0..), its step count nv and
+// the current block b.
 struct PfCursor {
-  int u, r, x, seq, nv, b;
+  int u, r, x, p0, n, row0, nv, b;
 };
 
 template <int KFMT, bool BALANCED>
@@ -136,16 +143,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
   u32x2* const lut = reinterpret_cast<u32x2*>(smem + kPfFp4Lut);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int H = a.heads, Q = a.qlen, HQ = H * Q;
-  const int32_t MM3_AS4* seq_s = (const int32_t MM3_AS4*)a.seq_lens;
+  const int H = a.heads;
   const int32_t MM3_AS4* bt_s = (const int32_t MM3_AS4*)a.bt;
 
   auto unit_at = [&](PfCursor& c, int u) {
     c.u = u;
     c.r = u / tiles;
     c.x = u - c.r * tiles;
-    c.seq = seq_s[c.r];
-    c.nv = tile_blocks(c.seq, c.x, H, Q, HQ);
+    const ReqRows q = req_rows<true>(a.rows, c.r);
+    c.p0 = q.p0;
+    c.n = q.n;
+    c.row0 = q.row0;
+    c.nv = routed(a.route, H, q.n) ? tile_blocks(q.p0, q.n, c.x, H) : 0;
+  };
+  // steps of unit v (any lane's own v)
+  auto unit_steps = [&](int v) {
+    const int r = v / tiles;
+    const ReqRows q = req_rows(a.rows, r);
+    return routed(a.route, H, q.n) ? tile_blocks(q.p0, q.n, v - r * tiles, H) : 0;
   };
   // next step of the list (callers guarantee one exists)
   auto advance = [&](PfCursor& c) {
@@ -165,10 +180,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     const int lo = (int)((int64_t)units * t / kPfThreads);
     const int hi = (int)((int64_t)units * (t + 1) / kPfThreads);
     int part = 0;
-    for (int v = lo; v < hi; ++v) {
-      const int r = v / tiles;
-      part += tile_blocks(a.seq_lens[r], v - r * tiles, H, Q, HQ);
-    }
+    for (int v = lo; v < hi; ++v) part += unit_steps(v);
     int incl = part;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -195,8 +207,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     if (part > 0 && pre <= s0 && s0 < pre + part) {
       int acc = pre;
       for (int v = lo; v < hi; ++v) {
-        const int r = v / tiles;
-        const int n = tile_blocks(a.seq_lens[r], v - r * tiles, H, Q, HQ);
+        const int n = unit_steps(v);
         if (s0 < acc + n) {
           scan[8] = v;
           scan[9] = (int)(s0 - acc);
@@ -223,6 +234,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
   int wave_pos_min = 0, wave_pos_max = -1;
   bool wave_live = false;
   auto load_q = [&]() __attribute__((always_inline)) {
+    const int HQ = H * cur.n;  // >= 1: the unit has steps
     const int wrow0 = cur.x * kPrefillRows + kPfWaveRows * wave;
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -230,8 +242,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
       const bool ok = i < HQ;
       const int ic = ok ? i : HQ - 1;
       const int j = ic / H, h = ic - j * H;
-      pos_q[qt] = ok ? cur.seq - Q + j : -1;
-      const uint16_t* qp = a.q + (int64_t)(cur.r * Q + j) * a.q_tok + (int64_t)h * a.q_head;
+      pos_q[qt] = ok ? cur.p0 + j : -1;
+      const uint16_t* qp = a.q + (int64_t)(cur.row0 + j) * a.q_tok + (int64_t)h * a.q_head;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const u32x4 v = ld16(qp + 16 * kk + 8 * kg);
@@ -250,8 +262,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
       }
     }
     wave_live = wrow0 < HQ;
-    wave_pos_min = cur.seq - Q + min(wrow0, HQ - 1) / H;
-    wave_pos_max = cur.seq - Q + min(wrow0 + kPfWaveRows - 1, HQ - 1) / H;
+    wave_pos_min = cur.p0 + min(wrow0, HQ - 1) / H;
+    wave_pos_max = cur.p0 + min(wrow0 + kPfWaveRows - 1, HQ - 1) / H;
     // land them now: a query load still pending at the loop would make the
     // compiler wait inside every step, and so on the copies in flight
     wait_vmcnt<0>();
@@ -378,6 +390,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
   auto flush = [&](int bfirst, int nst) __attribute__((always_inline)) {
     const int c = lane & 7;
     const int b = bfirst + c;
+    const int HQ = H * cur.n;
     // not unrolled: unrolled, the compiler keeps every row's address live
     // through the whole loop and spills
 #pragma unroll 1
@@ -386,8 +399,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
       const int i = cur.x * kPrefillRows + kPfWaveRows * wave + rho;
       if (c < nst && i < HQ) {
         const int j = i / H, h = i - j * H;
-        if (cur.seq - Q + j >= kBlock * b)
-          a.scores[(int64_t)h * a.s_head + (int64_t)(cur.r * Q + j) * a.s_row + b] =
+        if (cur.p0 + j >= kBlock * b)
+          a.scores[(int64_t)h * a.s_head + (int64_t)(cur.row0 + j) * a.s_row + b] =
               stage[rho * kPfStage + (c ^ (rho & 7))];
       }
     }
@@ -455,8 +468,8 @@ static int prefill_grid() {
 
 template <int KFMT>
 static hipError_t launch_prefill(const ScoreArgs& a, hipStream_t s) {
-  const int tiles = (a.heads * a.qlen + kPrefillRows - 1) / kPrefillRows;
-  const int64_t units = (int64_t)a.num_reqs * tiles;
+  const int tiles = (a.heads * a.rows.qlen + kPrefillRows - 1) / kPrefillRows;  // per request, at most
+  const int64_t units = (int64_t)a.rows.num_reqs * tiles;
   // the scan counts steps in 32-bit integers
   if (units <= kPfBalancedMaxUnits && units * a.nb_max <= INT32_MAX) {
     hipLaunchKernelGGL((prefill_score_kernel<KFMT, true>), dim3(prefill_grid<KFMT>()), dim3(kPfThreads), 0, s, a,

@@ -21,6 +21,7 @@
 // single-pass threshold select that needs no workspace.
 #include "mm3_device.h"
 #include "mm3_launch.h"
+#include "mm3_rows.h"
 
 namespace mm3 {
 
@@ -95,12 +96,11 @@ __device__ void select_generic(const float* srow, int nv, const TopkArgs& a, int
 template <int E>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int T = a.num_reqs * a.qlen;
   const int t = blockIdx.x * 4 + wave;
   const int h = blockIdx.y;
-  if (t >= T) return;
-  const int r = t / a.qlen, j = t - r * a.qlen;
-  const int pos = a.seq_lens[r] - a.qlen + j;
+  if (t >= a.rows.tokens) return;
+  const ReqRows rr = req_rows(a.rows, row_request(a.rows, t));
+  const int pos = rr.p0 + (t - rr.row0);
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)t * a.o_row;
   const int nv = pos < 0 ? 0 : pos / kBlock + 1;
   if (nv <= a.topk) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  const int T = a.num_reqs * a.qlen;
+  const int T = a.rows.tokens;
   dim3 grid((T + 3) / 4, a.heads), block(256);
   const int nb = a.nb_max;
   if (nb <= 64)
@@ -142,11 +142,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 
 __global__ __launch_bounds__(256) void sparse_table_kernel(SparseTableArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int T = a.num_reqs * a.qlen;
   const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const int r = t / a.qlen, j = t - r * a.qlen;
-  const int pos = a.seq_lens[r] - a.qlen + j;
+  if (t >= a.rows.tokens) return;
+  const int r = row_request(a.rows, t);
+  const ReqRows rr = req_rows(a.rows, r);
+  const int pos = rr.p0 + (t - rr.row0);
   const int32_t* ids = a.topk_idx + (int64_t)t * a.o_row;
   const int32_t* abt = a.abt + (int64_t)r * a.abt_row;
   int32_t* st = a.sparse + (int64_t)t * a.st_row;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void sparse_table_kernel(SparseTableArgs a) {
 }
 
 hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s) {
-  const int T = a.num_reqs * a.qlen;
+  const int T = a.rows.tokens;
   hipLaunchKernelGGL(sparse_table_kernel, dim3((T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }

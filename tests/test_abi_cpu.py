@@ -35,35 +35,53 @@ def test_exports_every_declared_symbol():
         assert re.search(rf"\bT {n}$", nm, re.M), f"{n} not a defined text symbol"
 
 
-def test_struct_layout_matches_header(tmp_path):
+@pytest.mark.parametrize("cname,cls", [("mm3_problem", B.Problem), ("mm3_rows", B.Rows)])
+def test_struct_layout_matches_header(tmp_path, cname, cls):
     src = tmp_path / "layout.c"
-    fields = [f[0] for f in B.Problem._fields_]
-    body = "".join(f'printf("%zu ", offsetof(mm3_problem, {f}));' for f in fields)
+    fields = [f[0] for f in cls._fields_]
+    body = "".join(f'printf("%zu ", offsetof({cname}, {f}));' for f in fields)
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mm3_index.h"\n'
-                   f'int main(void){{ {body} printf("%zu\\n", sizeof(mm3_problem)); return 0; }}\n')
+                   f'int main(void){{ {body} printf("%zu\\n", sizeof({cname})); return 0; }}\n')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
-    want = [getattr(B.Problem, f).offset for f in fields] + [ctypes.sizeof(B.Problem)]
+    want = [getattr(cls, f).offset for f in fields] + [ctypes.sizeof(cls)]
     assert got == want
 
 
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced
 
 
+ROW_FIELDS = {f[0] for f in B.Rows._fields_}
+
+
+def _rows(**kw):
+    m = B.Rows()
+    d = dict(seq_lens=FAKE * 4, cu_seqlens_q=None, prefix_lens=None, num_reqs=8, query_len=4,
+             total_q=None, max_seq_len=8192)
+    d.update(kw)
+    if d["total_q"] is None:
+        d["total_q"] = d["num_reqs"] * d["query_len"]
+    for k, v in d.items():
+        setattr(m, k, v)
+    return m
+
+
 def _problem(**kw):
     p = B.Problem()
     d = dict(q=FAKE, q_tok_stride=4 * 128, q_head_stride=128, heads=4, kfmt=0, kdata=FAKE * 2,
              kscales=None, num_pages=100, block_table=FAKE * 3, bt_row_stride=64, bt_width=64,
-             seq_lens=FAKE * 4, num_reqs=8, query_len=4, max_seq_len=8192, sm_scale=0.088)
-    d.update(kw)
+             sm_scale=0.088)
+    rk = {k: v for k, v in kw.items() if k in ROW_FIELDS}
+    d.update({k: v for k, v in kw.items() if k not in ROW_FIELDS})
     for k, v in d.items():
         setattr(p, k, v)
+    p.rows = _rows(**rk)
     return p
 
 
 def _score(p, sh=None, sr=64, sw=64, scores=FAKE * 5):
-    T = p.num_reqs * p.query_len
+    T = p.rows.total_q
     sh = T * sr if sh is None else sh
     return B.lib().mm3_index_score(ctypes.byref(p), scores, sh, sr, sw, None)
 
@@ -86,7 +104,7 @@ BAD_PROBLEMS = [
     ("no_pages", dict(num_pages=0), "page"),
     ("null_q", dict(q=None), "non-NULL"),
     ("null_table", dict(block_table=None), "non-NULL"),
-    ("null_lens", dict(seq_lens=None), "non-NULL"),
+    ("null_lens", dict(seq_lens=None), "seq_lens"),
     ("nvfp4_no_scales", dict(kfmt=1), "kscales"),
     ("q_misaligned", dict(q=FAKE + 8), "aligned"),
     ("k_misaligned", dict(kdata=FAKE * 2 + 4), "aligned"),
@@ -94,8 +112,13 @@ BAD_PROBLEMS = [
     ("q_head_overlap", dict(q_head_stride=64), "head stride"),
     ("table_narrow", dict(bt_width=63), "narrower"),
     ("table_row_stride", dict(bt_row_stride=32), "row stride"),
-    ("tokens_overflow", dict(num_reqs=1 << 20, query_len=1 << 12), "2^31"),
+    ("tokens_overflow", dict(num_reqs=1 << 20, query_len=1 << 12, total_q=0), "total_q"),
     ("rows_overflow", dict(heads=1 << 16, query_len=1 << 16, q_head_stride=128), "2^31"),
+    ("total_q_mismatch", dict(total_q=31), "total_q"),
+    ("total_q_negative", dict(cu_seqlens_q=FAKE * 8, total_q=-1), "total_q"),
+    ("prefix_without_cu", dict(prefix_lens=FAKE * 9), "prefix_lens needs cu_seqlens_q"),
+    ("cu_misaligned", dict(cu_seqlens_q=FAKE * 8 + 2), "aligned"),
+    ("prefix_misaligned", dict(cu_seqlens_q=FAKE * 8, prefix_lens=FAKE * 9 + 1), "aligned"),
 ]
 
 
@@ -128,18 +151,33 @@ def test_score_buffer_rules(label, kw, msg):
 def test_empty_batch_returns_ok_without_launch():
     assert _score(_problem(num_reqs=0)) == B.MM3_OK
     assert _err() == ""
-    rc = B.lib().mm3_index_topk(FAKE, 0, 64, 64, 4, FAKE * 4, 0, 4, 8192, 16, 1, 2, FAKE * 6, 0,
+    # ragged with no rows at all (every request empty)
+    assert _score(_problem(cu_seqlens_q=FAKE * 8, total_q=0)) == B.MM3_OK
+    rows = _rows(num_reqs=0)
+    rc = B.lib().mm3_index_topk(FAKE, 0, 64, 64, 4, ctypes.byref(rows), 16, 1, 2, FAKE * 6, 0,
                                 16, None)
     assert rc == B.MM3_OK
 
 
+def test_ragged_total_q_sizes_the_buffers():
+    """Ragged batches take total_q, not num_reqs * query_len, as the row count
+    that score and out strides must cover."""
+    p = _problem(cu_seqlens_q=FAKE * 8, prefix_lens=FAKE * 9, total_q=100, query_len=64)
+    # (only rejected calls here: a valid one would launch on the fake pointers)
+    assert _score(p, sh=99 * 64) == B.MM3_EINVAL and "head stride" in _err()
+    rows = _rows(cu_seqlens_q=FAKE * 8, total_q=100, query_len=64)
+    assert _topk(rows=rows, oh=99 * 16) == B.MM3_EINVAL and "head stride" in _err()
+
+
 def _topk(**kw):
-    d = dict(scores=FAKE, sh=32 * 64, sr=64, sw=64, heads=4, seq=FAKE * 4, R=8, Q=4, msl=8192,
-             topk=16, I=1, L=2, out=FAKE * 6, oh=32 * 16, orow=16)
+    rk = {k: kw.pop(k) for k in list(kw) if k in ROW_FIELDS}
+    d = dict(scores=FAKE, sh=32 * 64, sr=64, sw=64, heads=4, topk=16, I=1, L=2, out=FAKE * 6,
+             oh=32 * 16, orow=16, rows="default")
     d.update(kw)
-    return B.lib().mm3_index_topk(d["scores"], d["sh"], d["sr"], d["sw"], d["heads"], d["seq"],
-                                  d["R"], d["Q"], d["msl"], d["topk"], d["I"], d["L"], d["out"],
-                                  d["oh"], d["orow"], None)
+    rows = _rows(**rk) if d["rows"] == "default" else d["rows"]
+    return B.lib().mm3_index_topk(d["scores"], d["sh"], d["sr"], d["sw"], d["heads"],
+                                  None if rows is None else ctypes.byref(rows), d["topk"], d["I"],
+                                  d["L"], d["out"], d["oh"], d["orow"], None)
 
 
 BAD_TOPK = [
@@ -151,8 +189,11 @@ BAD_TOPK = [
     ("out_row_stride", dict(orow=8), "row stride"),
     ("out_head_stride", dict(oh=10), "head stride"),
     ("score_width", dict(sw=10, sr=10, sh=320), "width"),
-    ("null_seq", dict(seq=None), "seq_lens"),
+    ("null_seq", dict(seq_lens=None), "seq_lens"),
+    ("null_rows", dict(rows=None), "rows"),
     ("heads", dict(heads=0), "heads"),
+    ("prefix_without_cu", dict(prefix_lens=FAKE * 9), "prefix_lens"),
+    ("total_q", dict(total_q=33), "total_q"),
 ]
 
 
@@ -178,13 +219,14 @@ def test_decode_workspace_rules():
 
 
 def _sparse(**kw):
-    d = dict(ids=FAKE, orow=16, topk=16, seq=FAKE * 2, R=8, Q=4, msl=8192, abt=FAKE * 3, abt_row=128,
-             abt_w=128, P=2, stride=2, st=FAKE * 4, st_row=32, ctx=FAKE * 5)
+    rk = {k: kw.pop(k) for k in list(kw) if k in ROW_FIELDS}
+    d = dict(ids=FAKE, orow=16, topk=16, abt=FAKE * 3, abt_row=128, abt_w=128, P=2, stride=2,
+             st=FAKE * 4, st_row=32, ctx=FAKE * 5)
     d.update(kw)
-    return B.lib().mm3_build_sparse_block_table(d["ids"], d["orow"], d["topk"], d["seq"], d["R"],
-                                                d["Q"], d["msl"], d["abt"], d["abt_row"], d["abt_w"],
-                                                d["P"], d["stride"], d["st"], d["st_row"], d["ctx"],
-                                                None)
+    rows = _rows(**rk)
+    return B.lib().mm3_build_sparse_block_table(d["ids"], d["orow"], d["topk"], ctypes.byref(rows),
+                                                d["abt"], d["abt_row"], d["abt_w"], d["P"],
+                                                d["stride"], d["st"], d["st_row"], d["ctx"], None)
 
 
 BAD_SPARSE = [
@@ -194,6 +236,8 @@ BAD_SPARSE = [
     ("narrow_abt", dict(abt_w=127, abt_row=127), "narrower"),
     ("st_row", dict(st_row=31), "sparse table row stride"),
     ("pages", dict(P=0, stride=0), "pages_per_block"),
+    ("null_seq", dict(seq_lens=None), "seq_lens"),
+    ("total_q", dict(total_q=5), "total_q"),
 ]
 
 

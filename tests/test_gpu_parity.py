@@ -22,16 +22,20 @@ def _say(msg):
     print(msg, flush=True)
 
 
+def _ragged_kw(w):
+    return dict(cu_seqlens_q=w.cu_seqlens_q, prefix_lens=w.prefix_lens)
+
+
 def run_split(w, scores=None, out=None):
     """mm3_index_score then mm3_index_topk."""
     if scores is None:
         scores = torch.full((w.heads, w.rows, w.score_width), float("nan"), device=DEV)
     mm3.mm3_index_score(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
-                        w.sm_scale, kscales=w.kscales, scores=scores)
+                        w.sm_scale, kscales=w.kscales, scores=scores, **_ragged_kw(w))
     if out is None:
         out = torch.full((w.heads, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
     mm3.mm3_index_topk(scores, w.seq_lens, w.query_len, w.max_seq_len, w.topk, w.init_blocks,
-                       w.local_blocks, out=out)
+                       w.local_blocks, out=out, total_q=w.rows, **_ragged_kw(w))
     torch.cuda.synchronize()
     return scores, out
 
@@ -43,9 +47,19 @@ def run_fused(w, with_scores=True):
     out = torch.full((w.heads, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
     mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
                          w.sm_scale, w.topk, w.init_blocks, w.local_blocks, kscales=w.kscales,
-                         out=out, scores_out=scores)
+                         out=out, scores_out=scores, **_ragged_kw(w))
     torch.cuda.synchronize()
     return scores, out
+
+
+def _np(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def invariants(w, out):
+    P.check_invariants(out.cpu().numpy(), w.seq_lens.cpu().numpy(), w.query_len, w.topk,
+                       w.init_blocks, w.local_blocks, cu=_np(w.cu_seqlens_q),
+                       prefix=_np(w.prefix_lens))
 
 
 def full_check(w, scores, out, label):
@@ -53,7 +67,7 @@ def full_check(w, scores, out, label):
     s_ref, ids_ref = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
     err = P.check_scores(scores.cpu().numpy(), s_ref) if scores is not None else 0.0
     near = P.check_ids(out.cpu().numpy(), ids_ref, s_ref, a["seq_lens"], w.query_len, w.topk,
-                       w.init_blocks, w.local_blocks)
+                       w.init_blocks, w.local_blocks, cu=a["cu_seqlens_q"], prefix=a["prefix_lens"])
     _say(f"{label}: rows={w.rows} heads={w.heads} max score err={err:.3g} near-tie rows={near}")
     return near
 
@@ -381,3 +395,111 @@ def test_sparse_block_table_matches_oracle():
                                                     w.query_len, abt.cpu().numpy(), P_, stride)
         assert np.array_equal(st.cpu().numpy(), st_ref)
         assert np.array_equal(ctx.cpu().numpy(), ctx_ref)
+
+
+# ---------------------------------------------------------------- ragged
+#
+# cu_seqlens_q row offsets and optional prefix_lens (page "ops.index_topk",
+# minimax_m3_index_score / minimax_m3_index_topk).  A request with
+# heads * rows <= 16 goes to the decode scorer, a larger one to the prefill
+# scorer, in the same call.
+
+RAGGED = [
+    # (label, make kwargs)
+    ("decode_spec_rows", dict(R=12, lens=(500, 6000), Q=4, H=4, max_seq_len=8192, qlens=(0, 4))),
+    ("decode_h1_up_to_16", dict(R=9, lens=(100, 5000), Q=16, H=1, max_seq_len=8192, qlens=(1, 16),
+                                prefix="gap")),
+    ("prefill_chunks_gap", dict(R=4, lens=(900, 3000), Q=1024, H=4, max_seq_len=4096,
+                                qlens=[300, 0, 900, 77], prefix="gap")),
+    ("mixed_tail", dict(R=10, lens=(1300, 5000), Q=1200, H=4, max_seq_len=8192,
+                        qlens=[1, 2, 3, 4, 500, 0, 4, 1200, 2, 64], prefix="tail")),
+    ("mixed_no_prefix", dict(R=8, lens=(50, 4000), Q=700, H=2, max_seq_len=4096,
+                             qlens=[8, 9, 1, 700, 0, 5, 300, 8])),
+    ("mixed_rows_before_first_key", dict(R=5, lens=(0, 0), Q=600, H=1, max_seq_len=1024,
+                                         qlens=[600, 4, 16, 17, 3], fixed_lens=[100, 2, 700, 0, 3])),
+    ("empty_requests_at_ends", dict(R=6, lens=(200, 3000), Q=40, H=2, max_seq_len=4096,
+                                    qlens=[0, 0, 8, 40, 0, 0], prefix="gap")),
+    # more than 64 requests: the row -> request search takes two steps
+    ("many_requests_search", dict(R=300, lens=(1, 1500), Q=4, H=4, max_seq_len=2048, qlens=(0, 4),
+                                  prefix="tail")),
+    ("heads_over_16_all_prefill", dict(R=4, lens=(300, 2000), Q=9, H=17, max_seq_len=2048,
+                                       qlens=(1, 9))),
+    # more requests than the per-CU decode scorer holds: the chunked decode grid
+    ("decode_chunked_grid", dict(R=5000, lens=(1, 400), Q=2, H=1, max_seq_len=512, qlens=(0, 2))),
+]
+
+
+@pytest.mark.parametrize("kfmt", [KFMT_BF16, KFMT_NVFP4], ids=["bf16", "nvfp4"])
+@pytest.mark.parametrize("label,kw", RAGGED, ids=[e[0] for e in RAGGED])
+def test_ragged(label, kw, kfmt):
+    kw = dict(kw)
+    kw.setdefault("topk", 8)
+    w = make(name=label, I=1, L=2, kfmt=kfmt, seed=len(label) + kfmt, device=DEV, **kw)
+    _say(f"ragged {label} kfmt={kfmt}: R={w.num_reqs} rows={w.rows} bound={w.query_len}")
+    scores, out = run_split(w)
+    full_check(w, scores, out, label)
+    invariants(w, out)
+    s2, out2 = run_fused(w, with_scores=True)
+    assert torch.equal(out, out2), "fused ragged call differs from score + topk"
+    assert torch.equal(torch.nan_to_num(scores, nan=7.0), torch.nan_to_num(s2, nan=7.0))
+
+
+def test_ragged_equals_uniform_batch():
+    """A uniform batch given as cu_seqlens_q (and as prefix_lens = seq - Q)
+    must produce bit-identical scores and ids to the uniform call."""
+    w = config(2, device=DEV, R=16, lens=(900, 9000), max_seq_len=9216)
+    s_u, o_u = run_split(w)
+    cu = torch.arange(0, w.rows + 1, w.query_len, dtype=torch.int32, device=DEV)
+    for pre in [None, (w.seq_lens - w.query_len).to(torch.int32)]:
+        wr = w.__class__(**{**w.__dict__, "cu_seqlens_q": cu, "prefix_lens": pre})
+        s_r, o_r = run_split(wr)
+        assert torch.equal(o_u, o_r)
+        assert torch.equal(torch.nan_to_num(s_u, nan=7.0), torch.nan_to_num(s_r, nan=7.0))
+
+
+def test_ragged_sparse_block_table():
+    import oracle
+    w = make(name="ragged_sparse", R=7, lens=(300, 5000), Q=4, H=1, max_seq_len=8192, topk=8, I=1,
+             L=2, kfmt=KFMT_BF16, seed=41, device=DEV, qlens=(0, 4), prefix="gap")
+    _, out = run_fused(w, with_scores=False)
+    abt = torch.randint(0, 10**6, (w.num_reqs, w.nb_max * 2), dtype=torch.int32, device=DEV)
+    st, ctx = mm3.mm3_build_sparse_block_table(out, w.seq_lens, w.query_len, w.max_seq_len, abt, 1,
+                                               2, **_ragged_kw(w))
+    torch.cuda.synchronize()
+    st_ref, ctx_ref = oracle.sparse_block_table(out[0].cpu().numpy(), w.seq_lens.cpu().numpy(),
+                                                w.query_len, abt.cpu().numpy(), 1, 2,
+                                                cu_seqlens_q=_np(w.cu_seqlens_q),
+                                                prefix_lens=_np(w.prefix_lens))
+    assert np.array_equal(st.cpu().numpy(), st_ref)
+    assert np.array_equal(ctx.cpu().numpy(), ctx_ref)
+
+
+def test_full_size_mixed_serving():
+    """The ragged serving batch (64 speculative-decode requests and two
+    4096-row prefill chunks in one call): sampled decode requests whole and
+    sampled rows of both chunks against the oracle, the selection
+    invariants on every row."""
+    w = config(7, device=DEV)
+    _say(f"full mixed serving: R={w.num_reqs} rows={w.rows} H={w.heads}")
+    scores, out = run_fused(w, with_scores=True)
+    invariants(w, out)
+    _, out2 = run_split(w)
+    assert torch.equal(out, out2)
+    a, rows = host_subset(w, [0, 31, 63])
+    s_ref, ids_ref = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
+    err = P.check_scores(scores[:, rows].cpu().numpy(), s_ref)
+    near = P.check_ids(out[:, rows].cpu().numpy(), ids_ref, s_ref, a["seq_lens"], w.query_len,
+                       w.topk, w.init_blocks, w.local_blocks, cu=a["cu_seqlens_q"],
+                       prefix=a["prefix_lens"])
+    _say(f"mixed serving decode reqs: max err {err:.3g}, near-tie rows {near}")
+    rng = np.random.default_rng(7)
+    for r in [64, 65]:
+        a, rows = host_subset(w, [r])
+        loc = sorted(set([0, 127, 128, 4095] + rng.integers(0, 4096, 6).tolist()))
+        s_ref, ids_ref = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks,
+                                          rows=loc)
+        err = P.check_scores(scores[:, rows].cpu().numpy(), s_ref, rows=loc)
+        near = P.check_ids(out[:, rows].cpu().numpy(), ids_ref, s_ref, a["seq_lens"], w.query_len,
+                           w.topk, w.init_blocks, w.local_blocks, rows=loc, cu=a["cu_seqlens_q"],
+                           prefix=a["prefix_lens"])
+        _say(f"mixed serving chunk {r}: {len(loc)} sampled rows, max err {err:.3g}, near-tie rows {near}")

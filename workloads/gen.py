@@ -123,6 +123,11 @@ WORKLOADS = {
     # beyond the five: the chunked-prefill shape with NVFP4 keys
     6: dict(name="chunked_prefill_nvfp4", R=4, lens=(16384, 16384), Q=8192, H=4,
             max_seq_len=16384, topk=16, I=1, L=2, kfmt=KFMT_NVFP4),
+    # a ragged serving batch: 64 decode requests of 1..4 speculative rows and
+    # two 4096-token prefill chunks, in one call (cu_seqlens_q, prefix_lens)
+    7: dict(name="mixed_serving", R=66, lens=(4096, 32768), Q=4096, H=4,
+            max_seq_len=32768, topk=16, I=1, L=2, kfmt=KFMT_BF16,
+            qlens=[(1, 4)] * 64 + [4096, 4096], prefix="tail"),
 }
 
 
@@ -171,8 +176,9 @@ def make(name, R, lens, Q, H, max_seq_len, topk, I, L, kfmt, seed, device,
     q, k ~ N(0,1) rounded to bf16; NVFP4 keys are N(0,1) values encoded by
     _quantize_nvfp4.
 
-    Ragged batches: qlens gives each request's row count, as a list or as a
-    (lo, hi) range drawn uniformly per request; Q is then the bound on them
+    Ragged batches: qlens gives each request's row count, as one (lo, hi)
+    range drawn uniformly per request, or as a list of counts and ranges, one
+    per request; Q is then the bound on them
     (cu_seqlens_q holds the row offsets).  prefix: None (no prefix_lens: a
     request's rows are its last tokens), "tail" (prefix_lens = seq_len -
     rows, passed explicitly) or "gap" (prefix_lens = seq_len - rows - gap,
@@ -192,11 +198,12 @@ def make(name, R, lens, Q, H, max_seq_len, topk, I, L, kfmt, seed, device,
     assert max(seq_host + [0]) <= max_seq_len
     cu = pre = None
     if qlens is not None:
-        if isinstance(qlens, tuple):
-            nq = torch.randint(qlens[0], qlens[1] + 1, (R,), generator=g, device=dev).cpu().tolist()
-        else:
-            nq = [int(x) for x in qlens]
-            assert len(nq) == R
+        spec = [qlens] * R if isinstance(qlens, tuple) else list(qlens)
+        assert len(spec) == R
+        lo = torch.tensor([x[0] if isinstance(x, tuple) else int(x) for x in spec])
+        hi = torch.tensor([x[1] if isinstance(x, tuple) else int(x) for x in spec])
+        u = torch.rand((R,), generator=g, device=dev).cpu().double()
+        nq = (lo + (u * (hi - lo + 1).double()).floor().long().clamp(max=(hi - lo))).tolist()
         if prefix is not None:
             nq = [min(n, s) for n, s in zip(nq, seq_host)]
         assert max(nq + [0]) <= Q
