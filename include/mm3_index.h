@@ -176,6 +176,37 @@ int mm3_index_topk(const float* scores, int64_t s_head_stride,
                    int64_t o_row_stride, void* stream);
 
 /*
+ * Sparse block-table output: the attention pages of the selected blocks and
+ * each row's sparse context length, for ONE index head (page
+ * "ops.index_topk", minimax_m3_index_decode: attention_block_table,
+ * sparse_block_table_out, sparse_context_lens_out and block_page_stride,
+ * which come together).
+ *   attention_block_table  int32, request r's row at abt[r*abt_row_stride];
+ *              sparse block b owns entries [b*block_page_stride,
+ *              b*block_page_stride + pages_per_block);
+ *              abt_width >= cdiv(max_seq_len,128) * block_page_stride;
+ *              abt_row_stride >= abt_width.
+ *   pages_per_block P >= 1; block_page_stride in {P, 2P}.
+ *   sparse_table int32, row t at sparse_table[t*st_row_stride], st_row_stride
+ *              >= topk*P: slot j*P+i = abt[r][b_j*stride + i] for the row's
+ *              j-th id b_j, -1 for the slots of -1 ids.
+ *   sparse_ctx_lens int32 [total_q]: sum over the row's ids b of the tokens
+ *              of b it sees, min(128, pos - 128*b + 1); 0 when pos < 0.
+ * Every pointer 4-byte aligned.  Attention-table entries are read only for
+ * selected blocks.
+ */
+typedef struct mm3_sparse_out {
+    const int32_t* attention_block_table;
+    int64_t abt_row_stride;
+    int32_t abt_width;
+    int32_t pages_per_block;
+    int32_t block_page_stride;
+    int32_t* sparse_table;
+    int64_t st_row_stride;
+    int32_t* sparse_ctx_lens;
+} mm3_sparse_out;
+
+/*
  * Workspace bytes mm3_index_decode needs for this problem when it is given
  * no scores_out buffer (0 when scores_out is given).  Host-only, no HIP call.
  * Returns 0 and sets mm3_last_error() if p is invalid.
@@ -193,41 +224,28 @@ size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk,
  *   workspace   device memory of >= mm3_index_decode_workspace_bytes(),
  *               256-byte aligned (NULL allowed when that is 0).  Its contents
  *               need no initialisation; overlapping calls must not share it.
+ *   sparse      optional (NULL = none): the sparse block table of the
+ *               selected ids, built by the selector as it writes them (no
+ *               extra launch); needs heads == 1.
  */
 int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
                      int32_t local_blocks, int32_t* out, int64_t o_head_stride,
                      int64_t o_row_stride, float* scores_out,
                      int64_t s_head_stride, int64_t s_row_stride,
                      int32_t s_width, void* workspace, size_t workspace_bytes,
-                     void* stream);
+                     const mm3_sparse_out* sparse, void* stream);
 
 /*
- * mm3_build_sparse_block_table -- attention pages of the selected blocks, for
- * ONE index head (page "ops.index_topk", minimax_m3_index_decode: the
- * optional attention_block_table / sparse_block_table_out /
- * sparse_context_lens_out / block_page_stride arguments).
+ * mm3_build_sparse_block_table -- the sparse block table (mm3_sparse_out)
+ * of ids already selected, for ONE index head (page "ops.index_topk",
+ * minimax_m3_index_decode, the optional table arguments).
  *   topk_idx   int32 row t at topk_idx[t*o_row_stride], ids as mm3_index_topk
  *              writes them (ascending, -1 padded).
  *   rows       the batch's rows, as in mm3_problem.
- *   attention_block_table  int32, request r's row at abt[r*abt_row_stride];
- *              sparse block b owns entries [b*block_page_stride,
- *              b*block_page_stride + pages_per_block);
- *              abt_width >= cdiv(max_seq_len,128) * block_page_stride.
- *   pages_per_block P >= 1; block_page_stride in {P, 2P}.
- *   sparse_table int32, row t at sparse_table[t*st_row_stride], st_row_stride
- *              >= topk*P: slot j*P+i = abt[r][b_j*stride + i] for the j-th id,
- *              -1 for slots of -1 ids.
- *   sparse_ctx_lens int32 [total_q]: sum over selected b of the visible tokens
- *              of b, min(128, pos - 128*b + 1); 0 when pos < 0.
  */
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride,
                                  int32_t topk, const mm3_rows* rows,
-                                 const int32_t* attention_block_table,
-                                 int64_t abt_row_stride, int32_t abt_width,
-                                 int32_t pages_per_block,
-                                 int32_t block_page_stride,
-                                 int32_t* sparse_table, int64_t st_row_stride,
-                                 int32_t* sparse_ctx_lens, void* stream);
+                                 const mm3_sparse_out* sparse, void* stream);
 
 /* Message for the last non-OK return on this thread ("" if none).  Host
  * pointer, valid until the next call on this thread. */

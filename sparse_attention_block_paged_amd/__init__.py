@@ -2,6 +2,7 @@
 indexer hot path as a C-ABI HIP library (libmm3idx.so) with a thin ctypes
 binding.  PyTorch supplies device memory and streams only."""
 from ._binding import (BLOCK, HEAD_DIM, KFMT_BF16, KFMT_NVFP4, LIB_PATH, Mm3Error,
-                       Problem, Rows, decode_workspace_bytes, lib, make_problem, make_rows,
+                       Problem, Rows, SparseOut, decode_workspace_bytes, lib, make_problem,
+                       make_rows, make_sparse_out,
                        mm3_build_sparse_block_table, mm3_index_decode, mm3_index_score,
                        mm3_index_topk, score_width, version)

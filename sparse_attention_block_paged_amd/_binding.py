@@ -69,6 +69,19 @@ class Problem(ctypes.Structure):
     ]
 
 
+class SparseOut(ctypes.Structure):
+    _fields_ = [
+        ("attention_block_table", ctypes.c_void_p),
+        ("abt_row_stride", ctypes.c_int64),
+        ("abt_width", ctypes.c_int32),
+        ("pages_per_block", ctypes.c_int32),
+        ("block_page_stride", ctypes.c_int32),
+        ("sparse_table", ctypes.c_void_p),
+        ("st_row_stride", ctypes.c_int64),
+        ("sparse_ctx_lens", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -84,16 +97,16 @@ def lib():
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         PP = ctypes.POINTER(Problem)
         PR = ctypes.POINTER(Rows)
+        PS = ctypes.POINTER(SparseOut)
         L.mm3_index_score.argtypes = [PP, P, I64, I64, I32, P]
         L.mm3_index_score.restype = ctypes.c_int
         L.mm3_index_topk.argtypes = [P, I64, I64, I32, I32, PR, I32, I32, I32, P, I64, I64, P]
         L.mm3_index_topk.restype = ctypes.c_int
         L.mm3_index_decode_workspace_bytes.argtypes = [PP, I32, I32]
         L.mm3_index_decode_workspace_bytes.restype = SZ
-        L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, P]
+        L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, PS, P]
         L.mm3_index_decode.restype = ctypes.c_int
-        L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, PR, P, I64, I32, I32, I32, P, I64,
-                                                   P, P]
+        L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, PR, PS, P]
         L.mm3_build_sparse_block_table.restype = ctypes.c_int
         L.mm3_last_error.argtypes = []
         L.mm3_last_error.restype = ctypes.c_char_p
@@ -251,10 +264,43 @@ def decode_workspace_bytes(p: Problem, topk: int, with_scores_out: bool) -> int:
     return n
 
 
+def make_sparse_out(attention_block_table, pages_per_block, block_page_stride, sparse_table,
+                    sparse_ctx_lens) -> SparseOut:
+    """Marshal the sparse block-table outputs (all int32, contiguous rows)."""
+    for t in (attention_block_table, sparse_table, sparse_ctx_lens):
+        if t.dtype != torch.int32 or t.stride(-1) != 1:
+            raise ValueError("sparse-table tensors must be int32 with contiguous rows")
+    if attention_block_table.dim() != 2 or sparse_table.dim() != 2 or sparse_ctx_lens.dim() != 1:
+        raise ValueError("attention_block_table and sparse_table are 2-D, sparse_ctx_lens 1-D")
+    o = SparseOut()
+    o.attention_block_table = attention_block_table.data_ptr()
+    o.abt_row_stride = attention_block_table.stride(0)
+    o.abt_width = attention_block_table.shape[1]
+    o.pages_per_block = int(pages_per_block)
+    o.block_page_stride = int(block_page_stride)
+    o.sparse_table = sparse_table.data_ptr()
+    o.st_row_stride = sparse_table.stride(0)
+    o.sparse_ctx_lens = sparse_ctx_lens.data_ptr()
+    return o
+
+
 def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, topk,
                      init_blocks, local_blocks, kscales=None, out=None, scores_out=None,
-                     workspace=None, stream=None, cu_seqlens_q=None, prefix_lens=None):
-    """Scores then top-k in one call; returns out [heads, tokens, topk] int32."""
+                     workspace=None, stream=None, cu_seqlens_q=None, prefix_lens=None,
+                     attention_block_table=None, sparse_block_table_out=None,
+                     sparse_context_lens_out=None, pages_per_block=None, block_page_stride=None):
+    """Scores then top-k in one call; returns out [heads, tokens, topk] int32.
+    With the sparse-table arguments (all together, one index head) the
+    selector also writes sparse_block_table_out [tokens, >= topk * P] and
+    sparse_context_lens_out [tokens]."""
+    sp_args = (attention_block_table, sparse_block_table_out, sparse_context_lens_out,
+               pages_per_block, block_page_stride)
+    if any(x is not None for x in sp_args) and any(x is None for x in sp_args):
+        raise ValueError("sparse-table arguments must be provided together")
+    sparse = None
+    if attention_block_table is not None:
+        sparse = make_sparse_out(attention_block_table, pages_per_block, block_page_stride,
+                                 sparse_block_table_out, sparse_context_lens_out)
     p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales,
                      cu_seqlens_q, prefix_lens)
     H, T = q.shape[1], q.shape[0]
@@ -275,7 +321,9 @@ def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm
         sh = sr = sw = 0
     _check(lib().mm3_index_decode(ctypes.byref(p), int(topk), int(init_blocks), int(local_blocks),
                                   out.data_ptr(), out.stride(0), out.stride(1), _ptr(scores_out),
-                                  sh, sr, sw, ws_ptr, ws_bytes, _stream(q, stream)))
+                                  sh, sr, sw, ws_ptr, ws_bytes,
+                                  None if sparse is None else ctypes.byref(sparse),
+                                  _stream(q, stream)))
     return out
 
 
@@ -294,15 +342,13 @@ def mm3_build_sparse_block_table(topk_idx, seq_lens, query_len, max_seq_len,
         sparse_table = torch.empty((T, K * P), dtype=torch.int32, device=topk_idx.device)
     if sparse_ctx_lens is None:
         sparse_ctx_lens = torch.empty((T,), dtype=torch.int32, device=topk_idx.device)
-    for t in (topk_idx, attention_block_table, sparse_table, sparse_ctx_lens):
-        if t.dtype != torch.int32 or t.stride(-1) != 1:
-            raise ValueError("sparse-table tensors must be int32 with contiguous rows")
+    if topk_idx.dtype != torch.int32 or topk_idx.stride(-1) != 1:
+        raise ValueError("topk_idx must be int32 with contiguous rows")
     rows = make_rows(seq_lens, query_len, max_seq_len, T, cu_seqlens_q, prefix_lens)
+    sp = make_sparse_out(attention_block_table, P, block_page_stride, sparse_table, sparse_ctx_lens)
     _check(lib().mm3_build_sparse_block_table(
-        topk_idx.data_ptr(), topk_idx.stride(0), K, ctypes.byref(rows),
-        attention_block_table.data_ptr(), attention_block_table.stride(0),
-        attention_block_table.shape[1], P, int(block_page_stride), sparse_table.data_ptr(),
-        sparse_table.stride(0), sparse_ctx_lens.data_ptr(), _stream(topk_idx, stream)))
+        topk_idx.data_ptr(), topk_idx.stride(0), K, ctypes.byref(rows), ctypes.byref(sp),
+        _stream(topk_idx, stream)))
     return sparse_table, sparse_ctx_lens
 
 

@@ -130,6 +130,45 @@ int check_out(int32_t* out, int64_t oh, int64_t orow, int32_t heads, int64_t T, 
   return MM3_OK;
 }
 
+// The sparse-table output (page "ops.index_topk", minimax_m3_index_decode:
+// the table arguments come together, one index head, page stride P or 2P,
+// the attention table wide enough for every block).
+int check_sparse(const mm3_sparse_out* s, const mm3_rows* rows, int32_t topk, int32_t heads) {
+  if (!s->attention_block_table || !s->sparse_table || !s->sparse_ctx_lens)
+    return fail(MM3_EINVAL, "sparse-table arguments must be provided together (non-NULL)");
+  if (heads != 1)
+    return fail(MM3_EINVAL, "the sparse block table is built for one index head, got %d", heads);
+  const int32_t P = s->pages_per_block;
+  if (P < 1) return fail(MM3_EINVAL, "pages_per_block must be >= 1");
+  if (s->block_page_stride != P && s->block_page_stride != 2 * P)
+    return fail(MM3_EINVAL, "block_page_stride must be P or 2P (P=%d), got %d", P, s->block_page_stride);
+  const int64_t nb = cdiv64(rows->max_seq_len, MM3_BLOCK);
+  if ((int64_t)s->abt_width < nb * s->block_page_stride)
+    return fail(MM3_EINVAL, "attention block table narrower than cdiv(max_seq_len,128)*stride");
+  if (rows->num_reqs > 1 && s->abt_row_stride < s->abt_width)
+    return fail(MM3_EINVAL, "attention block table row stride must be >= its width");
+  if (s->abt_row_stride < 0 || s->st_row_stride < 0)
+    return fail(MM3_EINVAL, "sparse-table strides must be non-negative");
+  if (rows->total_q > 1 && s->st_row_stride < (int64_t)topk * P)
+    return fail(MM3_EINVAL, "sparse table row stride must be >= topk * pages_per_block");
+  if (!aligned(s->sparse_table, 4) || !aligned(s->sparse_ctx_lens, 4) ||
+      !aligned(s->attention_block_table, 4))
+    return fail(MM3_EINVAL, "int32 buffers must be 4-byte aligned");
+  return MM3_OK;
+}
+
+SparseOut sparse_of(const mm3_sparse_out* s) {
+  SparseOut o{};
+  o.abt = s->attention_block_table;
+  o.abt_row = s->abt_row_stride;
+  o.table = s->sparse_table;
+  o.st_row = s->st_row_stride;
+  o.ctx_lens = s->sparse_ctx_lens;
+  o.pages_per_block = s->pages_per_block;
+  o.block_page_stride = s->block_page_stride;
+  return o;
+}
+
 Rows rows_of(const mm3_rows* m) {
   Rows r{};
   r.seq_lens = m->seq_lens;
@@ -276,12 +315,13 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
                      int32_t local_blocks, int32_t* out, int64_t o_head_stride,
                      int64_t o_row_stride, float* scores_out, int64_t s_head_stride,
                      int64_t s_row_stride, int32_t s_width, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, const mm3_sparse_out* sparse, void* stream) {
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
   const int64_t T = p->rows.total_q;
   if ((rc = check_out(out, o_head_stride, o_row_stride, p->heads, T, topk))) return rc;
+  if (sparse && (rc = check_sparse(sparse, &p->rows, topk, p->heads))) return rc;
   float* s = scores_out;
   int64_t sh = s_head_stride, sr = s_row_stride;
   int32_t sw = s_width;
@@ -302,51 +342,34 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   if (p->rows.max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
   TopkArgs a = topk_args(s, sh, sr, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
                          o_head_stride, o_row_stride);
+  if (sparse) {
+    a.sp = sparse_of(sparse);
+    a.sparse = 1;
+  }
   hipError_t e = launch_topk(a, st);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
 }
 
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, int32_t topk,
-                                 const mm3_rows* rows, const int32_t* attention_block_table,
-                                 int64_t abt_row_stride, int32_t abt_width,
-                                 int32_t pages_per_block, int32_t block_page_stride,
-                                 int32_t* sparse_table, int64_t st_row_stride,
-                                 int32_t* sparse_ctx_lens, void* stream) {
-  if (!topk_idx || !attention_block_table || !sparse_table || !sparse_ctx_lens)
+                                 const mm3_rows* rows, const mm3_sparse_out* sparse, void* stream) {
+  if (!topk_idx || !sparse)
     return fail(MM3_EINVAL, "sparse-table arguments must be provided together (non-NULL)");
   if (topk < 1 || topk > MM3_MAX_TOPK) return fail(MM3_EINVAL, "topk must be in [1, 1024]");
   int rc = check_rows(rows, 0);
   if (rc) return rc;
-  const int64_t nb = cdiv64(rows->max_seq_len, MM3_BLOCK);
-  if (pages_per_block < 1) return fail(MM3_EINVAL, "pages_per_block must be >= 1");
-  if (block_page_stride != pages_per_block && block_page_stride != 2 * pages_per_block)
-    return fail(MM3_EINVAL, "block_page_stride must be P or 2P (P=%d), got %d", pages_per_block,
-                block_page_stride);
-  if ((int64_t)abt_width < nb * block_page_stride)
-    return fail(MM3_EINVAL, "attention block table narrower than cdiv(max_seq_len,128)*stride");
-  if (rows->num_reqs > 1 && abt_row_stride < abt_width)
-    return fail(MM3_EINVAL, "attention block table row stride must be >= its width");
+  if ((rc = check_sparse(sparse, rows, topk, 1))) return rc;
   const int64_t T = rows->total_q;
   if (T > 1 && o_row_stride < topk) return fail(MM3_EINVAL, "topk row stride must be >= topk");
-  if (T > 1 && st_row_stride < (int64_t)topk * pages_per_block)
-    return fail(MM3_EINVAL, "sparse table row stride must be >= topk * pages_per_block");
-  if (!aligned(topk_idx, 4) || !aligned(sparse_table, 4) || !aligned(sparse_ctx_lens, 4) ||
-      !aligned(attention_block_table, 4))
-    return fail(MM3_EINVAL, "int32 buffers must be 4-byte aligned");
+  if (o_row_stride < 0) return fail(MM3_EINVAL, "topk row stride must be non-negative");
+  if (!aligned(topk_idx, 4)) return fail(MM3_EINVAL, "int32 buffers must be 4-byte aligned");
   if (T == 0) return ok();
   SparseTableArgs a{};
   a.topk_idx = topk_idx;
   a.o_row = o_row_stride;
   a.rows = rows_of(rows);
-  a.abt = attention_block_table;
-  a.abt_row = abt_row_stride;
-  a.sparse = sparse_table;
-  a.st_row = st_row_stride;
-  a.ctx_lens = sparse_ctx_lens;
+  a.sp = sparse_of(sparse);
   a.topk = topk;
-  a.pages_per_block = pages_per_block;
-  a.block_page_stride = block_page_stride;
   hipError_t e = launch_sparse_table(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sparse-table launch");
   return ok();

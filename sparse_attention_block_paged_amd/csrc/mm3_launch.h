@@ -49,6 +49,17 @@ struct ScoreArgs {
   float sm_scale;
 };
 
+// Sparse block-table output (one index head).
+struct SparseOut {
+  const int32_t* abt;
+  int64_t abt_row;
+  int32_t* table;
+  int64_t st_row;
+  int32_t* ctx_lens;
+  int32_t pages_per_block;
+  int32_t block_page_stride;
+};
+
 struct TopkArgs {
   const float* scores;
   int64_t s_head;
@@ -62,20 +73,16 @@ struct TopkArgs {
   int32_t init_blocks;
   int32_t local_blocks;
   int32_t nb_max;
+  SparseOut sp;   // used when sparse != 0 (heads == 1)
+  int32_t sparse;
 };
 
 struct SparseTableArgs {
   const int32_t* topk_idx;
   int64_t o_row;
   Rows rows;
-  const int32_t* abt;
-  int64_t abt_row;
-  int32_t* sparse;
-  int64_t st_row;
-  int32_t* ctx_lens;
+  SparseOut sp;
   int32_t topk;
-  int32_t pages_per_block;
-  int32_t block_page_stride;
 };
 
 // Each returns hipSuccess or the launch error.

@@ -35,9 +35,28 @@ __device__ __forceinline__ uint32_t block_key(const float* srow, int b, int nv, 
   return order_key(srow[b]);
 }
 
+// Writes a selected id at its output slot and, with a sparse table, the
+// block's attention pages at the same slot; each lane sums the context
+// tokens of the ids it wrote.
+template <bool SPARSE>
+struct Emit {
+  int32_t* orow;
+  const int32_t* abt;  // the request's attention-table row
+  int32_t* st;         // the row's sparse-table row
+  int P, stride, pos;
+  int len;
+  __device__ __forceinline__ void operator()(int slot, int id) {
+    orow[slot] = id;
+    if constexpr (SPARSE) {
+      for (int i = 0; i < P; ++i) st[slot * P + i] = abt[(int64_t)id * stride + i];
+      len += min(kBlock, pos - kBlock * id + 1);
+    }
+  }
+};
+
 // E keys per lane in registers: rows with nv <= 64*E.
-template <int E>
-__device__ void select_regs(const float* srow, int nv, const TopkArgs& a, int32_t* orow, int lane) {
+template <int E, typename EmitT>
+__device__ void select_regs(const float* srow, int nv, const TopkArgs& a, EmitT& emit, int lane) {
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = block_key(srow, 64 * e + lane, nv, a.init_blocks, a.local_blocks);
@@ -60,14 +79,15 @@ __device__ void select_regs(const float* srow, int nv, const TopkArgs& a, int32_
     const uint64_t tmask = __ballot(key[e] == T);
     const bool sel = key[e] > T || (key[e] == T && tie_base + lanes_below(tmask) < need);
     const uint64_t smask = __ballot(sel);
-    if (sel) orow[base + lanes_below(smask)] = 64 * e + lane;
+    if (sel) emit(base + lanes_below(smask), 64 * e + lane);
     base += __popcll(smask);
     tie_base += __popcll(tmask);
   }
 }
 
 // Any nv: keys re-read from the score row on every pass.
-__device__ void select_generic(const float* srow, int nv, const TopkArgs& a, int32_t* orow, int lane) {
+template <typename EmitT>
+__device__ void select_generic(const float* srow, int nv, const TopkArgs& a, EmitT& emit, int lane) {
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
@@ -87,49 +107,84 @@ __device__ void select_generic(const float* srow, int nv, const TopkArgs& a, int
     const uint64_t tmask = __ballot(k == T);
     const bool sel = k > T || (k == T && tie_base + lanes_below(tmask) < need);
     const uint64_t smask = __ballot(sel);
-    if (sel) orow[base + lanes_below(smask)] = b0 + lane;
+    if (sel) emit(base + lanes_below(smask), b0 + lane);
     base += __popcll(smask);
     tie_base += __popcll(tmask);
   }
 }
 
-template <int E>
+// SPARSE: also the row's sparse block table (one index head, page
+// "ops.index_topk", minimax_m3_index_decode: table construction fused into
+// the selector).
+template <int E, bool SPARSE>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   const int h = blockIdx.y;
   if (t >= a.rows.tokens) return;
-  const ReqRows rr = req_rows(a.rows, row_request(a.rows, t));
+  const int r = row_request(a.rows, t);
+  const ReqRows rr = req_rows(a.rows, r);
   const int pos = rr.p0 + (t - rr.row0);
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)t * a.o_row;
   const int nv = pos < 0 ? 0 : pos / kBlock + 1;
+  Emit<SPARSE> emit{orow, nullptr, nullptr, 0, 0, pos, 0};
+  if constexpr (SPARSE) {
+    emit.abt = a.sp.abt + (int64_t)r * a.sp.abt_row;
+    emit.st = a.sp.table + (int64_t)t * a.sp.st_row;
+    emit.P = a.sp.pages_per_block;
+    emit.stride = a.sp.block_page_stride;
+  }
   if (nv <= a.topk) {
+    // every visible block, then -1
     for (int k = lane; k < a.topk; k += 64) orow[k] = k < nv ? k : -1;
+    if constexpr (SPARSE) {
+      const int P = emit.P;
+      for (int x = lane; x < a.topk * P; x += 64) {
+        const int k = x / P, i = x - k * P;
+        emit.st[x] = k < nv ? emit.abt[(int64_t)k * emit.stride + i] : -1;
+      }
+      if (lane == 0) a.sp.ctx_lens[t] = pos + 1 > 0 ? pos + 1 : 0;  // all of blocks 0..pos/128
+    }
     return;
   }
   const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
   if (E > 0)
-    select_regs<(E > 0 ? E : 1)>(srow, nv, a, orow, lane);
+    select_regs<(E > 0 ? E : 1)>(srow, nv, a, emit, lane);
   else
-    select_generic(srow, nv, a, orow, lane);
+    select_generic(srow, nv, a, emit, lane);
+  if constexpr (SPARSE) {
+    // nv > topk: all topk slots hold ids, no padding
+    int len = emit.len;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) len += __shfl_xor(len, off, 64);
+    if (lane == 0) a.sp.ctx_lens[t] = len;
+  }
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+template <bool SPARSE>
+static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
   const int T = a.rows.tokens;
   dim3 grid((T + 3) / 4, a.heads), block(256);
   const int nb = a.nb_max;
   if (nb <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<1, SPARSE>), grid, block, 0, s, a);
   else if (nb <= 128)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<2, SPARSE>), grid, block, 0, s, a);
   else if (nb <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<4, SPARSE>), grid, block, 0, s, a);
   else if (nb <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<8, SPARSE>), grid, block, 0, s, a);
   else if (nb <= 1024)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<16, SPARSE>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(topk_kernel<0>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<0, SPARSE>), grid, block, 0, s, a);
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.sparse)
+    launch_topk_t<true>(a, s);
+  else
+    launch_topk_t<false>(a, s);
   return hipGetLastError();
 }
 
@@ -148,13 +203,13 @@ __global__ __launch_bounds__(256) void sparse_table_kernel(SparseTableArgs a) {
   const ReqRows rr = req_rows(a.rows, r);
   const int pos = rr.p0 + (t - rr.row0);
   const int32_t* ids = a.topk_idx + (int64_t)t * a.o_row;
-  const int32_t* abt = a.abt + (int64_t)r * a.abt_row;
-  int32_t* st = a.sparse + (int64_t)t * a.st_row;
-  const int P = a.pages_per_block, slots = a.topk * P;
+  const int32_t* abt = a.sp.abt + (int64_t)r * a.sp.abt_row;
+  int32_t* st = a.sp.table + (int64_t)t * a.sp.st_row;
+  const int P = a.sp.pages_per_block, slots = a.topk * P;
   for (int x = lane; x < slots; x += 64) {
     const int k = x / P, i = x - k * P;
     const int b = ids[k];
-    st[x] = b < 0 ? -1 : abt[(int64_t)b * a.block_page_stride + i];
+    st[x] = b < 0 ? -1 : abt[(int64_t)b * a.sp.block_page_stride + i];
   }
   int len = 0;
   for (int k = lane; k < a.topk; k += 64) {
@@ -163,7 +218,7 @@ __global__ __launch_bounds__(256) void sparse_table_kernel(SparseTableArgs a) {
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) len += __shfl_xor(len, off, 64);
-  if (lane == 0) a.ctx_lens[t] = len;
+  if (lane == 0) a.sp.ctx_lens[t] = len;
 }
 
 hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s) {

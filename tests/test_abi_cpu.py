@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol():
         assert re.search(rf"\bT {n}$", nm, re.M), f"{n} not a defined text symbol"
 
 
-@pytest.mark.parametrize("cname,cls", [("mm3_problem", B.Problem), ("mm3_rows", B.Rows)])
+@pytest.mark.parametrize("cname,cls", [("mm3_problem", B.Problem), ("mm3_rows", B.Rows),
+                                       ("mm3_sparse_out", B.SparseOut)])
 def test_struct_layout_matches_header(tmp_path, cname, cls):
     src = tmp_path / "layout.c"
     fields = [f[0] for f in cls._fields_]
@@ -129,7 +130,7 @@ def test_problem_rules(label, kw, msg):
     assert msg in _err(), _err()
     # the same rule guards the fused entry point
     rc = B.lib().mm3_index_decode(ctypes.byref(p), 16, 1, 2, FAKE * 6, 32 * 16, 16, None, 0, 0, 0,
-                                  FAKE * 7, 1 << 30, None)
+                                  FAKE * 7, 1 << 30, None, None)
     assert rc == B.MM3_EINVAL
 
 
@@ -210,7 +211,7 @@ def test_decode_workspace_rules():
     assert B.lib().mm3_index_decode_workspace_bytes(ctypes.byref(p), 16, 1) == 0
     for ws, nbytes in [(None, need), (FAKE * 7, need - 1), (FAKE * 7 + 16, need)]:
         rc = B.lib().mm3_index_decode(ctypes.byref(p), 16, 1, 2, FAKE * 6, 32 * 16, 16, None, 0, 0,
-                                      0, ws, nbytes, None)
+                                      0, ws, nbytes, None, None)
         assert rc == B.MM3_EWORKSPACE, (ws, nbytes)
         assert "workspace" in _err()
     bad = _problem(heads=0)
@@ -218,15 +219,27 @@ def test_decode_workspace_rules():
     assert "heads" in _err()
 
 
+def _sparse_out(abt=FAKE * 3, abt_row=128, abt_w=128, P=2, stride=2, st=FAKE * 4, st_row=32,
+                ctx=FAKE * 5):
+    o = B.SparseOut()
+    o.attention_block_table, o.abt_row_stride, o.abt_width = abt, abt_row, abt_w
+    o.pages_per_block, o.block_page_stride = P, stride
+    o.sparse_table, o.st_row_stride, o.sparse_ctx_lens = st, st_row, ctx
+    return o
+
+
+SPARSE_KEYS = ("abt", "abt_row", "abt_w", "P", "stride", "st", "st_row", "ctx")
+
+
 def _sparse(**kw):
     rk = {k: kw.pop(k) for k in list(kw) if k in ROW_FIELDS}
-    d = dict(ids=FAKE, orow=16, topk=16, abt=FAKE * 3, abt_row=128, abt_w=128, P=2, stride=2,
-             st=FAKE * 4, st_row=32, ctx=FAKE * 5)
+    sk = {k: kw.pop(k) for k in list(kw) if k in SPARSE_KEYS}
+    d = dict(ids=FAKE, orow=16, topk=16)
     d.update(kw)
     rows = _rows(**rk)
+    sp = _sparse_out(**sk)
     return B.lib().mm3_build_sparse_block_table(d["ids"], d["orow"], d["topk"], ctypes.byref(rows),
-                                                d["abt"], d["abt_row"], d["abt_w"], d["P"],
-                                                d["stride"], d["st"], d["st_row"], d["ctx"], None)
+                                                ctypes.byref(sp), None)
 
 
 BAD_SPARSE = [
@@ -257,3 +270,35 @@ def test_binding_rejects_wrong_dtypes_before_the_library():
         mm3.make_problem(q, k, bt, sl, 4, 2048, 0.1)
     with pytest.raises(ValueError):
         mm3.make_problem(q.bfloat16(), k, bt.long(), sl, 4, 2048, 0.1)
+
+
+FUSED_SPARSE_BAD = [
+    ("heads", dict(), dict(), "one index head"),
+    ("missing_ctx", dict(heads=1, q_head_stride=128), dict(ctx=None), "together"),
+    ("stride", dict(heads=1, q_head_stride=128), dict(stride=3), "block_page_stride"),
+    ("narrow_abt", dict(heads=1, q_head_stride=128), dict(abt_w=127, abt_row=127), "narrower"),
+    ("st_row", dict(heads=1, q_head_stride=128), dict(st_row=31), "row stride"),
+]
+
+
+@pytest.mark.parametrize("label,pkw,skw,msg", FUSED_SPARSE_BAD, ids=[b[0] for b in FUSED_SPARSE_BAD])
+def test_fused_sparse_table_rules(label, pkw, skw, msg):
+    """The fused call's sparse-table output (page "ops.index_topk",
+    minimax_m3_index_decode: arguments together, one index head, stride P or
+    2P) is checked before anything is enqueued."""
+    p = _problem(**pkw)
+    sp = _sparse_out(**skw)
+    rc = B.lib().mm3_index_decode(ctypes.byref(p), 16, 1, 2, FAKE * 6, 32 * 16, 16, None, 0, 0, 0,
+                                  FAKE * 7, 1 << 30, ctypes.byref(sp), None)
+    assert rc == B.MM3_EINVAL
+    assert msg in _err(), _err()
+
+
+def test_binding_sparse_arguments_together():
+    import torch
+    z = torch.zeros((4, 16), dtype=torch.int32)
+    with pytest.raises(ValueError, match="together"):
+        mm3.mm3_index_decode(torch.zeros((4, 1, 128), dtype=torch.bfloat16),
+                             torch.zeros((2, 128, 128), dtype=torch.bfloat16), z[:1],
+                             torch.zeros((1,), dtype=torch.int32), 4, 2048, 0.1, 4, 1, 1,
+                             attention_block_table=z)

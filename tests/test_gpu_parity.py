@@ -503,3 +503,54 @@ def test_full_size_mixed_serving():
                            w.topk, w.init_blocks, w.local_blocks, rows=loc, cu=a["cu_seqlens_q"],
                            prefix=a["prefix_lens"])
         _say(f"mixed serving chunk {r}: {len(loc)} sampled rows, max err {err:.3g}, near-tie rows {near}")
+
+
+# ------------------------------------------------- fused sparse block table
+#
+# page "ops.index_topk", minimax_m3_index_decode: the optional sparse-table
+# arguments fuse table construction into the selector (one index head).
+
+FUSED_SPARSE = [
+    # (label, make kwargs, pages per block, page stride)
+    ("uniform_p1", dict(R=6, lens=(1, 9000), Q=4, H=1, max_seq_len=9216, topk=16), 1, 1),
+    ("uniform_p2_stride4", dict(R=6, lens=(1, 9000), Q=4, H=1, max_seq_len=9216, topk=16), 2, 4),
+    ("uniform_p8_stride16", dict(R=4, lens=(100, 30000), Q=2, H=1, max_seq_len=32768, topk=16), 8, 16),
+    ("short_rows_before_zero", dict(R=5, lens=(1, 3), Q=4, H=1, max_seq_len=512, topk=4), 2, 2),
+    ("generic_selector", dict(R=2, lens=(140000, 160000), Q=1, H=1, max_seq_len=163840, topk=16), 2, 4),
+    ("ragged_gap", dict(R=9, lens=(100, 9000), Q=8, H=1, max_seq_len=9216, topk=8, qlens=(0, 8),
+                        prefix="gap"), 2, 2),
+    ("ragged_mixed_prefill", dict(R=4, lens=(1000, 4000), Q=300, H=1, max_seq_len=4096, topk=8,
+                                  qlens=[3, 300, 0, 17], prefix="tail"), 1, 2),
+]
+
+
+@pytest.mark.parametrize("label,kw,P_,stride", FUSED_SPARSE, ids=[e[0] for e in FUSED_SPARSE])
+def test_fused_sparse_block_table(label, kw, P_, stride):
+    import oracle
+    w = make(name=label, I=1, L=2, kfmt=KFMT_BF16, seed=len(label) + 5, device=DEV, **kw)
+    _say(f"fused sparse {label}: R={w.num_reqs} rows={w.rows} P={P_} stride={stride}")
+    abt = torch.randint(0, 10**6, (w.num_reqs, w.nb_max * stride), dtype=torch.int32, device=DEV)
+    st = torch.full((w.rows, w.topk * P_ + 3), -7, dtype=torch.int32, device=DEV)[:, : w.topk * P_]
+    ctx = torch.full((w.rows,), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((1, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
+    mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                         w.sm_scale, w.topk, w.init_blocks, w.local_blocks, out=out,
+                         attention_block_table=abt, sparse_block_table_out=st,
+                         sparse_context_lens_out=ctx, pages_per_block=P_, block_page_stride=stride,
+                         **_ragged_kw(w))
+    torch.cuda.synchronize()
+    # ids as without the table, and as the oracle selects them
+    _, out_plain = run_fused(w, with_scores=False)
+    assert torch.equal(out, out_plain)
+    full_check(w, None, out, label)
+    st_ref, ctx_ref = oracle.sparse_block_table(out[0].cpu().numpy(), w.seq_lens.cpu().numpy(),
+                                                w.query_len, abt.cpu().numpy(), P_, stride,
+                                                cu_seqlens_q=_np(w.cu_seqlens_q),
+                                                prefix_lens=_np(w.prefix_lens))
+    assert np.array_equal(st.cpu().numpy(), st_ref)
+    assert np.array_equal(ctx.cpu().numpy(), ctx_ref)
+    # and as the standalone builder writes it
+    st2, ctx2 = mm3.mm3_build_sparse_block_table(out, w.seq_lens, w.query_len, w.max_seq_len, abt,
+                                                 P_, stride, **_ragged_kw(w))
+    torch.cuda.synchronize()
+    assert torch.equal(st2, st.contiguous()) and torch.equal(ctx2, ctx)
