@@ -57,6 +57,8 @@ int check_rows(const mm3_rows* m, int32_t heads) {
     return fail(MM3_EINVAL, "seq_lens, cu_seqlens_q and prefix_lens must be 4-byte aligned");
   if ((int64_t)heads * m->query_len > INT32_MAX)
     return fail(MM3_EINVAL, "heads * query_len must be below 2^31");
+  if (m->num_reqs == 0 && m->total_q != 0)
+    return fail(MM3_EINVAL, "total_q must be 0 without requests, got %d", m->total_q);
   if (!m->cu_seqlens_q) {
     if (m->prefix_lens) return fail(MM3_EINVAL, "prefix_lens needs cu_seqlens_q");
     if ((int64_t)m->num_reqs * m->query_len != m->total_q)

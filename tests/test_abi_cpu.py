@@ -118,6 +118,7 @@ BAD_PROBLEMS = [
     ("total_q_mismatch", dict(total_q=31), "total_q"),
     ("total_q_negative", dict(cu_seqlens_q=FAKE * 8, total_q=-1), "total_q"),
     ("prefix_without_cu", dict(prefix_lens=FAKE * 9), "prefix_lens needs cu_seqlens_q"),
+    ("ragged_rows_without_requests", dict(cu_seqlens_q=FAKE * 8, num_reqs=0, total_q=5), "without requests"),
     ("cu_misaligned", dict(cu_seqlens_q=FAKE * 8 + 2), "aligned"),
     ("prefix_misaligned", dict(cu_seqlens_q=FAKE * 8, prefix_lens=FAKE * 9 + 1), "aligned"),
 ]

@@ -424,7 +424,9 @@ RAGGED = [
                                   prefix="tail")),
     ("heads_over_16_all_prefill", dict(R=4, lens=(300, 2000), Q=9, H=17, max_seq_len=2048,
                                        qlens=(1, 9))),
-    # more requests than the per-CU decode scorer holds: the chunked decode grid
+    # the most requests the per-CU decode scorer holds in LDS, and one more
+    # than that: the chunked decode grid
+    ("decode_cu_max_requests", dict(R=4096, lens=(1, 300), Q=2, H=1, max_seq_len=512, qlens=(0, 2))),
     ("decode_chunked_grid", dict(R=5000, lens=(1, 400), Q=2, H=1, max_seq_len=512, qlens=(0, 2))),
 ]
 
@@ -554,3 +556,50 @@ def test_fused_sparse_block_table(label, kw, P_, stride):
                                                  P_, stride, **_ragged_kw(w))
     torch.cuda.synchronize()
     assert torch.equal(st2, st.contiguous()) and torch.equal(ctx2, ctx)
+
+
+def test_graph_capture_replay_ragged():
+    """Capture a ragged mixed call once (fixed total_q and row bound); replays
+    after rewriting cu_seqlens_q, prefix_lens, seq_lens and q in place match
+    eager calls."""
+    w = make(name="graph_ragged", R=6, lens=(1500, 6000), Q=600, H=2, max_seq_len=8192, topk=8,
+             I=1, L=2, kfmt=KFMT_BF16, seed=51, device=DEV, qlens=[1, 600, 3, 0, 200, 8],
+             prefix="tail")
+    out = torch.full((w.heads, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
+    p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                         w.sm_scale, **_ragged_kw(w))
+    ws = torch.empty(mm3.decode_workspace_bytes(p, w.topk, False), dtype=torch.uint8, device=DEV)
+    call = lambda: mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                        w.max_seq_len, w.sm_scale, w.topk, w.init_blocks,
+                                        w.local_blocks, out=out, workspace=ws, **_ragged_kw(w))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    rng = np.random.default_rng(5)
+    T = w.rows
+    for it in range(4):
+        # new split of the same T rows over the 6 requests (each <= 600), new
+        # lengths and prefixes with prefix + rows <= seq_len <= 6000
+        while True:
+            cuts = np.sort(rng.integers(0, T + 1, 5))
+            n = np.diff(np.concatenate([[0], cuts, [T]]))
+            if n.max() <= w.query_len:
+                break
+        seq = rng.integers(n.max(), 6001, 6)
+        seq = np.maximum(seq, n)
+        pre = seq - n - rng.integers(0, 50, 6)
+        pre = np.maximum(pre, 0)
+        w.cu_seqlens_q.copy_(torch.from_numpy(np.concatenate([[0], np.cumsum(n)]).astype(np.int32)))
+        w.prefix_lens.copy_(torch.from_numpy(pre.astype(np.int32)))
+        w.seq_lens.copy_(torch.from_numpy(seq.astype(np.int32)))
+        w.q.copy_(torch.randn(w.q.shape, device=DEV).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        _, want = run_fused(w, with_scores=False)
+        assert torch.equal(got, want), f"replay {it} differs from eager"
+        invariants(w, got)
