@@ -9,7 +9,7 @@
 // batch).
 //
 // Design.  Decode is a bandwidth-bound GEMV: every key (256 B bf16, 72 B
-// NVFP4) is read once and serves all H*Q rows of its request.  One wavefront
+// NVFP4) is read once and serves all H*n rows of its request.  One wavefront
 // scores one page (= one block) at a time:
 //   * the page is loaded straight into MFMA A-operand registers with 16-byte
 //     loads: lane l takes token 16*tt + l%16 and 16 contiguous bytes of it,
@@ -20,11 +20,13 @@
 //   * the block maximum is an in-register max over each lane's 4 tokens per
 //     tile and 8 tiles, masked only on a causally partial block, then a
 //     2-step cross-lane max (lanes l, l^16, l^32).
-// The grid is (block chunks, requests), sized from max_seq_len so it is
-// fixed under graph capture; chunks past a request's end return at once.
-// Unlike the pages' Triton split-K kernel there is no per-chunk partial
-// result: a block's score is complete inside one wave, so the split needs no
-// merge.
+// The default grid is one workgroup per CU, each taking an equal slice of
+// the batch's (request, block) pairs (decode_score_cu); above 4096 requests
+// or 2 GiB of scores, a grid of (block chunks, requests) sized from
+// max_seq_len (decode_score_chunked).  Both grids depend on host arguments
+// only, so they are fixed under graph capture.  Unlike the pages' Triton
+// split-K kernel there is no per-chunk partial result: a block's score is
+// complete inside one wave, so the split needs no merge.
 #include "mm3_device.h"
 #include "mm3_fp4.h"
 #include "mm3_launch.h"
@@ -266,7 +268,7 @@ __device__ __forceinline__ int64_t page_of(const ScoreArgs& a, int r, int b) {
 // page stream makes every later wait on page data wait for that store too.
 // Each wave keeps up to kStage (row, block) scores -- value and byte offset --
 // in its own LDS area and writes them out when the area is full (every
-// kStage / (H*Q) blocks, rare) and once after its last page load, with
+// kStage / (H*n) blocks, rare) and once after its last page load, with
 // consecutive blocks of a row on adjacent lanes.
 constexpr int kStage = 512;
 
