@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--copies", type=int, default=2, help="page-pool copies rotated per step")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (step_ms_graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU work for the oracle baseline")
@@ -250,6 +252,25 @@ def main():
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
 
+    # the same step captured once per pool copy and replayed: the library
+    # enqueues fixed grids with no allocation, so a step captures whole
+    ms_graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(side):
+            for c in range(len(copies)):
+                step(c)  # eager once on the capture stream
+            torch.cuda.synchronize()
+            for c in range(len(copies)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(c)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        ms_graph = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps, args.warmup)
+
     # kernels alone, on the same stream (HIP events), same inputs
     ms_score = timed(score_only, max(args.steps, 20), 3)
     ms_topk = timed(topk_only, max(args.steps, 20), 3)
@@ -332,6 +353,7 @@ def main():
         "roofline": roof,
         "selector": dict(kernel="topk_kernel", ms=round(ms_topk, 4),
                          achieved_gbs=round(sel_gbs, 1), bytes=alg["selector_bytes"]),
+        "step_ms_graph": None if ms_graph is None else round(ms_graph, 5),
         "scorer_ms_p10_p50_p90": pct_score,
         "scorer_ms_warm": round(ms_score_warm, 4),
         "hbm_copy_measured_gbs": copy_gbs,
