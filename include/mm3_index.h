@@ -176,6 +176,26 @@ int mm3_index_topk(const float* scores, int64_t s_head_stride,
                    int64_t o_row_stride, void* stream);
 
 /*
+ * mm3_index_topk_blocks -- the selection of mm3_index_topk with each row's
+ * visible-block count given directly instead of derived from its position
+ * (page "indexer_nvfp4", MiniMaxM3IndexerRocmNvfp4Impl: the prefill selector
+ * takes the row block counts the metadata builder materialises,
+ * num_valid_pages).
+ *   row_blocks int32 [total_q], contiguous: nv of row t, in
+ *              [0, cdiv(max_seq_len,128)] (a device precondition, not
+ *              checked); the row's scores are read for blocks b < nv.
+ *   Forced blocks, ordering, padding, out and the stride rules as in
+ *   mm3_index_topk.
+ */
+int mm3_index_topk_blocks(const float* scores, int64_t s_head_stride,
+                          int64_t s_row_stride, int32_t s_width, int32_t heads,
+                          const int32_t* row_blocks, int32_t total_q,
+                          int32_t max_seq_len, int32_t topk,
+                          int32_t init_blocks, int32_t local_blocks,
+                          int32_t* out, int64_t o_head_stride,
+                          int64_t o_row_stride, void* stream);
+
+/*
  * Sparse block-table output: the attention pages of the selected blocks and
  * each row's sparse context length, for ONE index head (page
  * "ops.index_topk", minimax_m3_index_decode: attention_block_table,

@@ -27,7 +27,7 @@ BLOCK = 128
 HEAD_DIM = 128
 
 EXPORTED = (
-    "mm3_index_score", "mm3_index_topk", "mm3_index_decode_workspace_bytes",
+    "mm3_index_score", "mm3_index_topk", "mm3_index_topk_blocks", "mm3_index_decode_workspace_bytes",
     "mm3_index_decode", "mm3_build_sparse_block_table", "mm3_last_error",
     "mm3_version",
 )
@@ -102,6 +102,9 @@ def lib():
         L.mm3_index_score.restype = ctypes.c_int
         L.mm3_index_topk.argtypes = [P, I64, I64, I32, I32, PR, I32, I32, I32, P, I64, I64, P]
         L.mm3_index_topk.restype = ctypes.c_int
+        L.mm3_index_topk_blocks.argtypes = [P, I64, I64, I32, I32, P, I32, I32, I32, I32, I32, P,
+                                            I64, I64, P]
+        L.mm3_index_topk_blocks.restype = ctypes.c_int
         L.mm3_index_decode_workspace_bytes.argtypes = [PP, I32, I32]
         L.mm3_index_decode_workspace_bytes.restype = SZ
         L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, PS, P]
@@ -253,6 +256,29 @@ def mm3_index_topk(scores, seq_lens, query_len, max_seq_len, topk, init_blocks, 
                                 scores.shape[2], H, ctypes.byref(rows), int(topk), int(init_blocks),
                                 int(local_blocks), out.data_ptr(), out.stride(0), out.stride(1),
                                 _stream(scores, stream)))
+    return out
+
+
+def mm3_index_topk_blocks(scores, row_blocks, max_seq_len, topk, init_blocks, local_blocks,
+                          out=None, stream=None):
+    """Block ids [heads, tokens, topk] int32 with each row's visible-block
+    count taken from row_blocks (int32 [tokens] on the device)."""
+    H = scores.shape[0]
+    if row_blocks.dtype != torch.int32 or row_blocks.dim() != 1 or not row_blocks.is_contiguous():
+        raise ValueError("row_blocks must be contiguous int32 [tokens]")
+    T = row_blocks.shape[0]
+    if out is None:
+        out = torch.empty((H, T, topk), dtype=torch.int32, device=scores.device)
+    if scores.dtype != torch.float32 or scores.stride(2) != 1:
+        raise ValueError("scores must be fp32 with unit column stride")
+    if out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1 or out.shape[2] != topk \
+            or out.shape[0] != H or out.shape[1] < T:
+        raise ValueError("out must be int32 [heads, >=tokens, topk] with unit column stride")
+    _check(lib().mm3_index_topk_blocks(scores.data_ptr(), scores.stride(0), scores.stride(1),
+                                       scores.shape[2], H, row_blocks.data_ptr(), T,
+                                       int(max_seq_len), int(topk), int(init_blocks),
+                                       int(local_blocks), out.data_ptr(), out.stride(0),
+                                       out.stride(1), _stream(scores, stream)))
     return out
 
 

@@ -303,6 +303,50 @@ int mm3_index_topk(const float* scores, int64_t s_head_stride, int64_t s_row_str
   return ok();
 }
 
+int mm3_index_topk_blocks(const float* scores, int64_t s_head_stride, int64_t s_row_stride,
+                          int32_t s_width, int32_t heads, const int32_t* row_blocks,
+                          int32_t total_q, int32_t max_seq_len, int32_t topk, int32_t init_blocks,
+                          int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                          int64_t o_row_stride, void* stream) {
+  if (heads < 1) return fail(MM3_EINVAL, "heads must be >= 1");
+  if (total_q < 0) return fail(MM3_EINVAL, "total_q must be >= 0, got %d", total_q);
+  if (max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
+  const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
+  if (nb > MM3_MAX_BLOCKS)
+    return fail(MM3_EINVAL, "cdiv(max_seq_len,128) = %lld must be below 65535", (long long)nb);
+  int rc = check_select(topk, init_blocks, local_blocks);
+  if (rc) return rc;
+  if (!row_blocks) return fail(MM3_EINVAL, "row_blocks must be non-NULL");
+  if (!aligned(row_blocks, 4)) return fail(MM3_EINVAL, "row_blocks must be 4-byte aligned");
+  const int64_t T = total_q;
+  if (!scores) return fail(MM3_EINVAL, "scores must be non-NULL");
+  if (!aligned(scores, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
+  if (s_width < nb) return fail(MM3_EINVAL, "score width < cdiv(max_seq_len,128)");
+  if (s_head_stride < 0 || s_row_stride < 0) return fail(MM3_EINVAL, "score strides must be non-negative");
+  if (T > 1 && s_row_stride < s_width) return fail(MM3_EINVAL, "score row stride must be >= score width");
+  if (heads > 1 && s_head_stride < T * s_row_stride)
+    return fail(MM3_EINVAL, "score head stride must be >= tokens * row stride");
+  if ((rc = check_out(out, o_head_stride, o_row_stride, heads, T, topk))) return rc;
+  if (T == 0) return ok();
+  TopkArgs a{};
+  a.scores = scores;
+  a.s_head = s_head_stride;
+  a.s_row = s_row_stride;
+  a.rows.tokens = total_q;  // rows map unused: nv comes from row_blocks
+  a.out = out;
+  a.o_head = o_head_stride;
+  a.o_row = o_row_stride;
+  a.heads = heads;
+  a.topk = topk;
+  a.init_blocks = init_blocks;
+  a.local_blocks = local_blocks;
+  a.nb_max = (int32_t)nb;
+  a.row_blocks = row_blocks;
+  hipError_t e = launch_topk(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
 size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk, int32_t with_scores_out) {
   if (check_problem(p)) return 0;
   if (check_select(topk, 0, 0)) return 0;

@@ -75,6 +75,7 @@ struct TopkArgs {
   int32_t nb_max;
   SparseOut sp;   // used when sparse != 0 (heads == 1)
   int32_t sparse;
+  const int32_t* row_blocks;  // when set: nv per row, instead of rows' positions
 };
 
 struct SparseTableArgs {

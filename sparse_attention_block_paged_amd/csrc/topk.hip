@@ -122,11 +122,16 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int t = blockIdx.x * 4 + wave;
   const int h = blockIdx.y;
   if (t >= a.rows.tokens) return;
-  const int r = row_request(a.rows, t);
-  const ReqRows rr = req_rows(a.rows, r);
-  const int pos = rr.p0 + (t - rr.row0);
+  int r = 0, pos = -1, nv;
+  if (a.row_blocks != nullptr) {
+    nv = a.row_blocks[t];  // given per row (never with a sparse table)
+  } else {
+    r = row_request(a.rows, t);
+    const ReqRows rr = req_rows(a.rows, r);
+    pos = rr.p0 + (t - rr.row0);
+    nv = pos < 0 ? 0 : pos / kBlock + 1;
+  }
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)t * a.o_row;
-  const int nv = pos < 0 ? 0 : pos / kBlock + 1;
   Emit<SPARSE> emit{orow, nullptr, nullptr, 0, 0, pos, 0};
   if constexpr (SPARSE) {
     emit.abt = a.sp.abt + (int64_t)r * a.sp.abt_row;

@@ -303,3 +303,29 @@ def test_binding_sparse_arguments_together():
                              torch.zeros((2, 128, 128), dtype=torch.bfloat16), z[:1],
                              torch.zeros((1,), dtype=torch.int32), 4, 2048, 0.1, 4, 1, 1,
                              attention_block_table=z)
+
+
+def _topk_blocks(**kw):
+    d = dict(scores=FAKE, sh=32 * 64, sr=64, sw=64, heads=4, rb=FAKE * 4, T=32, msl=8192,
+             topk=16, I=1, L=2, out=FAKE * 6, oh=32 * 16, orow=16)
+    d.update(kw)
+    return B.lib().mm3_index_topk_blocks(d["scores"], d["sh"], d["sr"], d["sw"], d["heads"], d["rb"],
+                                         d["T"], d["msl"], d["topk"], d["I"], d["L"], d["out"],
+                                         d["oh"], d["orow"], None)
+
+
+BAD_TOPK_BLOCKS = [
+    ("null_blocks", dict(rb=None), "row_blocks"),
+    ("blocks_misaligned", dict(rb=FAKE * 4 + 2), "aligned"),
+    ("negative_rows", dict(T=-1), "total_q"),
+    ("forced_exceed", dict(topk=4, I=3, L=2, orow=4, oh=128), "exceeds"),
+    ("score_width", dict(sw=10, sr=10, sh=320), "width"),
+    ("head_stride", dict(sh=31 * 64), "head stride"),
+    ("out_row_stride", dict(orow=8), "row stride"),
+]
+
+
+@pytest.mark.parametrize("label,kw,msg", BAD_TOPK_BLOCKS, ids=[b[0] for b in BAD_TOPK_BLOCKS])
+def test_topk_blocks_rules(label, kw, msg):
+    assert _topk_blocks(**kw) == B.MM3_EINVAL
+    assert msg in _err(), _err()

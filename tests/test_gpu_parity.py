@@ -603,3 +603,47 @@ def test_graph_capture_replay_ragged():
         _, want = run_fused(w, with_scores=False)
         assert torch.equal(got, want), f"replay {it} differs from eager"
         invariants(w, got)
+
+
+# ------------------------------------------- selection by row block counts
+#
+# page "indexer_nvfp4", MiniMaxM3IndexerRocmNvfp4Impl: the prefill selector
+# takes each row's visible-block count (num_valid_pages).  The oracle's
+# selection for a row of nv blocks is its selection for a one-row request
+# whose row sits at position 128 (nv - 1) (no row for nv = 0).
+
+def _oracle_by_blocks(s, nv, topk, I, L):
+    import oracle
+    seq = np.where(nv > 0, 128 * (nv.astype(np.int64) - 1) + 1, 0).astype(np.int32)
+    return oracle.topk(s, seq, 1, topk, I, L)
+
+
+@pytest.mark.parametrize("H,T,nb,topk,I,L", [(1, 300, 64, 16, 1, 2), (4, 257, 256, 16, 1, 2),
+                                             (2, 130, 1100, 32, 2, 3), (1, 64, 40, 40, 0, 0)])
+def test_topk_blocks_matches_oracle(H, T, nb, topk, I, L):
+    g = torch.Generator(device=DEV).manual_seed(T + nb)
+    W = -(-nb // 16) * 16
+    s = torch.randint(-40, 40, (H, T, W), generator=g, device=DEV).float() * 0.25  # ties
+    nv = torch.randint(0, nb + 1, (T,), generator=g, device=DEV).to(torch.int32)
+    nv[:3] = torch.tensor([0, 1, nb], dtype=torch.int32)
+    out = torch.full((H, T, topk), -7, dtype=torch.int32, device=DEV)
+    mm3.mm3_index_topk_blocks(s, nv, 128 * nb, topk, I, L, out=out)
+    torch.cuda.synchronize()
+    want = _oracle_by_blocks(s.cpu().numpy(), nv.cpu().numpy(), topk, I, L)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_topk_blocks_equals_position_selection():
+    """On a ragged batch, selecting with row_blocks = each row's nv gives the
+    ids mm3_index_topk derives from positions."""
+    w = make(name="by_blocks", R=6, lens=(200, 5000), Q=300, H=2, max_seq_len=8192, topk=16, I=1,
+             L=2, kfmt=KFMT_BF16, seed=61, device=DEV, qlens=[4, 300, 0, 17, 1, 120], prefix="gap")
+    scores, out = run_split(w)
+    pos = P.row_positions(w.seq_lens.cpu().numpy(), w.query_len, _np(w.cu_seqlens_q),
+                          _np(w.prefix_lens))
+    nv = torch.from_numpy(np.where(pos >= 0, pos // 128 + 1, 0).astype(np.int32)).to(DEV)
+    out2 = torch.full_like(out, -7)
+    mm3.mm3_index_topk_blocks(scores, nv, w.max_seq_len, w.topk, w.init_blocks, w.local_blocks,
+                              out=out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
