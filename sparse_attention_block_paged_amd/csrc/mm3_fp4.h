@@ -24,7 +24,7 @@ constexpr int64_t e4m3_units9(int c) {
 
 // E4M3 code (no sign) nearest to p * 2^-10, ties to even code, saturating.
 constexpr int e4m3_code_from_units10(int64_t p) {
-  int code;
+  int code = 0;
   if (p < 16) {  // below the smallest normal: grid step 2 units
     int64_t q = p >> 1;
     if (p & 1) q += (q & 1);
