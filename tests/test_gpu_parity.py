@@ -189,6 +189,7 @@ EDGE = [
     ("big_topk", dict(R=3, lens=(5000, 40000), Q=2, H=1, max_seq_len=65536, topk=300, I=3, L=5)),
     ("hq_16_boundary", dict(R=4, lens=(500, 4000), Q=2, H=8, max_seq_len=4096, topk=16, I=1, L=2)),
     ("hq_17_prefill_path", dict(R=3, lens=(500, 4000), Q=17, H=1, max_seq_len=4096, topk=16, I=1, L=2)),
+    ("heads_17_q1", dict(R=3, lens=(500, 4000), Q=1, H=17, max_seq_len=4096, topk=16, I=1, L=2)),
     ("q1_h1", dict(R=7, lens=(1, 9000), Q=1, H=1, max_seq_len=9216, topk=16, I=1, L=2)),
     ("generic_selector_long", dict(R=2, lens=(140000, 160000), Q=1, H=1, max_seq_len=163840,
                                    topk=16, I=1, L=2)),
@@ -647,3 +648,51 @@ def test_topk_blocks_equals_position_selection():
                               out=out2)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+# ------------------------------------------------------------ maximum sizes
+
+def test_max_blocks_single_request():
+    """cdiv(max_seq_len, 128) = 65534, the largest the pages allow: one
+    request at the maximum length (2 GiB of pages), two decode rows.  Both
+    rows against the oracle (every block), and the generic selector over
+    65534 blocks."""
+    L = 65534 * 128 - 5
+    w = make(name="max_blocks", R=1, lens=(L, L), Q=2, H=1, max_seq_len=65534 * 128, topk=16, I=1,
+             L=2, kfmt=KFMT_BF16, seed=71, device=DEV)
+    _say(f"max blocks: nb_max={w.nb_max} pages={w.kdata.shape[0]}")
+    scores, out = run_fused(w, with_scores=True)
+    _, out2 = run_split(w)
+    assert torch.equal(out, out2)
+    full_check(w, scores, out, "max_blocks")
+    invariants(w, out)
+
+
+def test_topk_1024():
+    """The largest topk, on rows with more visible blocks than that."""
+    w = make(name="topk_1024", R=3, lens=(131072 + 300, 200000), Q=2, H=1, max_seq_len=200064,
+             topk=1024, I=4, L=8, kfmt=KFMT_BF16, seed=72, device=DEV)
+    scores, out = run_fused(w, with_scores=True)
+    full_check(w, scores, out, "topk_1024")
+    invariants(w, out)
+
+
+def test_scores_past_2gib_use_direct_stores():
+    """A score tensor whose extent passes 2 GiB (a wide head stride) takes the
+    chunked decode grid with direct stores; its scores and ids equal those of
+    a compact tensor."""
+    w = config(2, device=DEV, R=8, lens=(900, 6000), max_seq_len=8192)
+    s_ref, o_ref = run_split(w)
+    sh = (1 << 28) + 64  # floats: the last head starts past 2 GiB (3 GiB extent)
+    buf = torch.full(((w.heads - 1) * sh + w.rows * w.score_width,), float("nan"), device=DEV)
+    big = buf.as_strided((w.heads, w.rows, w.score_width), (sh, w.score_width, 1))
+    mm3.mm3_index_score(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                        w.sm_scale, scores=big)
+    out = torch.full_like(o_ref, -7)
+    mm3.mm3_index_topk(big, w.seq_lens, w.query_len, w.max_seq_len, w.topk, w.init_blocks,
+                       w.local_blocks, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(big, nan=7.0), torch.nan_to_num(s_ref, nan=7.0))
+    assert torch.equal(out, o_ref)
+    del buf, big
+    torch.cuda.empty_cache()
