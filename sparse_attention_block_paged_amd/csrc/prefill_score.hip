@@ -156,11 +156,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     c.row0 = q.row0;
     c.nv = routed(a.route, H, q.n) ? tile_blocks(q.p0, q.n, c.x, H) : 0;
   };
-  // steps of unit v (any lane's own v)
+  // steps of unit v (any lane's own v); a lane walks its units in order, so
+  // it keeps the last request's rows and loads each request once
+  int memo_r = -1;
+  ReqRows memo_q{0, 0, 0};
+  bool memo_routed = false;
   auto unit_steps = [&](int v) {
     const int r = v / tiles;
-    const ReqRows q = req_rows(a.rows, r);
-    return routed(a.route, H, q.n) ? tile_blocks(q.p0, q.n, v - r * tiles, H) : 0;
+    if (r != memo_r) {
+      memo_r = r;
+      memo_q = req_rows(a.rows, r);
+      memo_routed = routed(a.route, H, memo_q.n);
+    }
+    return memo_routed ? tile_blocks(memo_q.p0, memo_q.n, v - r * tiles, H) : 0;
   };
   // next step of the list (callers guarantee one exists)
   auto advance = [&](PfCursor& c) {
