@@ -102,3 +102,30 @@ def test_planted_score_mistakes_are_caught(case):
     g[tuple(inv)] = 0.0  # write outside the visible set
     with pytest.raises(AssertionError):
         P.check_scores(g, s)
+
+
+def test_row_positions_hand_worked():
+    """Positions of a uniform and of a ragged batch, written out by hand."""
+    seq = np.array([10, 3], dtype=np.int32)
+    assert P.row_positions(seq, 4).tolist() == [6, 7, 8, 9, -1, 0, 1, 2]
+    cu = np.array([0, 2, 2, 5], dtype=np.int32)
+    seq3 = np.array([10, 7, 300], dtype=np.int32)
+    # no prefix: each request's rows are its last tokens
+    assert P.row_positions(seq3, 8, cu).tolist() == [8, 9, 297, 298, 299]
+    pre = np.array([4, 0, 128], dtype=np.int32)
+    assert P.row_positions(seq3, 8, cu, pre).tolist() == [4, 5, 128, 129, 130]
+
+
+def test_ragged_checkers_catch_a_shifted_position():
+    """On a ragged batch the invariant checker uses the ragged positions: ids
+    computed for positions one block later must fail it."""
+    from workloads import make
+    w = make(name="rg", R=3, lens=(700, 3000), Q=300, H=1, max_seq_len=4096, topk=4, I=1, L=1,
+             kfmt=0, seed=3, device="cpu", qlens=[2, 300, 5], prefix="tail")
+    a = host_arrays(w)
+    s, ids = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
+    P.check_invariants(ids, a["seq_lens"], w.query_len, w.topk, w.init_blocks, w.local_blocks,
+                       cu=a["cu_seqlens_q"], prefix=a["prefix_lens"])
+    with pytest.raises(AssertionError):
+        P.check_invariants(ids, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
+                           w.local_blocks, cu=a["cu_seqlens_q"], prefix=a["prefix_lens"] + 128)
