@@ -492,6 +492,11 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs
   int32_t* r0s = smem + 2 * R + 1;  // [R]
   const int per = (R + NT - 1) / NT;
   const int r0 = min(R, (int)threadIdx.x * per), r1 = min(R, r0 + per);
+  // the table load goes out first, so its latency overlaps the length loads'
+  u32x2 lut_v{0u, 0u};
+  if constexpr (KFMT == 1) {
+    if (threadIdx.x < 256) lut_v = lut_entry();
+  }
   int sum = 0;
   for (int r = r0; r < r1; ++r) {
     const ReqRows q = req_rows(a.rows, r);
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs
     sum += req_blocks(packed_p0(v), packed_n(v));
   }
   if constexpr (KFMT == 1) {
-    if (threadIdx.x < 256) fill_lut(lut);
+    if (threadIdx.x < 256) lut[threadIdx.x] = lut_v;
   }
   // exclusive scan of the partial sums: within each wave by lane shifts,
   // then over the wave totals (two barriers in all)

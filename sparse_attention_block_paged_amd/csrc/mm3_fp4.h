@@ -80,10 +80,12 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t x, u32x2 tab) {
   return r;
 }
 
-// Copy the table into LDS (threads 0..255 one entry each).
-__device__ __forceinline__ void fill_lut(u32x2* lut) {
-  lut[threadIdx.x].x = kFp4Lut.w[threadIdx.x][0];
-  lut[threadIdx.x].y = kFp4Lut.w[threadIdx.x][1];
+// This thread's table entry (threads 0..255 one entry each).
+__device__ __forceinline__ u32x2 lut_entry() {
+  return u32x2{kFp4Lut.w[threadIdx.x][0], kFp4Lut.w[threadIdx.x][1]};
 }
+
+// Copy the table into LDS (threads 0..255 one entry each).
+__device__ __forceinline__ void fill_lut(u32x2* lut) { lut[threadIdx.x] = lut_entry(); }
 
 }  // namespace mm3
