@@ -239,12 +239,14 @@ int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStr
   return e == hipSuccess ? MM3_OK : hip_fail(e, "scorer launch");
 }
 
-TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t heads, const mm3_rows* rows,
-                   int32_t topk, int32_t I, int32_t L, int32_t* out, int64_t oh, int64_t orow) {
+TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t sw, int32_t heads,
+                   const mm3_rows* rows, int32_t topk, int32_t I, int32_t L, int32_t* out, int64_t oh,
+                   int64_t orow) {
   TopkArgs a{};
   a.scores = s;
   a.s_head = sh;
   a.s_row = sr;
+  a.s_width = sw;
   a.rows = rows_of(rows);
   a.out = out;
   a.o_head = oh;
@@ -296,8 +298,8 @@ int mm3_index_topk(const float* scores, int64_t s_head_stride, int64_t s_row_str
     return fail(MM3_EINVAL, "score head stride must be >= tokens * row stride");
   if ((rc = check_out(out, o_head_stride, o_row_stride, heads, T, topk))) return rc;
   if (T == 0) return ok();
-  TopkArgs a = topk_args(scores, s_head_stride, s_row_stride, heads, rows, topk, init_blocks,
-                         local_blocks, out, o_head_stride, o_row_stride);
+  TopkArgs a = topk_args(scores, s_head_stride, s_row_stride, s_width, heads, rows, topk,
+                         init_blocks, local_blocks, out, o_head_stride, o_row_stride);
   hipError_t e = launch_topk(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
@@ -332,6 +334,7 @@ int mm3_index_topk_blocks(const float* scores, int64_t s_head_stride, int64_t s_
   a.scores = scores;
   a.s_head = s_head_stride;
   a.s_row = s_row_stride;
+  a.s_width = s_width;
   a.rows.tokens = total_q;  // rows map unused: nv comes from row_blocks
   a.out = out;
   a.o_head = o_head_stride;
@@ -386,7 +389,7 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   if (T == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
   if (p->rows.max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
-  TopkArgs a = topk_args(s, sh, sr, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
+  TopkArgs a = topk_args(s, sh, sr, sw, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
                          o_head_stride, o_row_stride);
   if (sparse) {
     a.sp = sparse_of(sparse);

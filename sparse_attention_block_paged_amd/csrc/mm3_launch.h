@@ -64,6 +64,7 @@ struct TopkArgs {
   const float* scores;
   int64_t s_head;
   int64_t s_row;
+  int32_t s_width;  // columns of a score row (reads stay below it)
   Rows rows;
   int32_t* out;
   int64_t o_head;

@@ -29,10 +29,15 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-__device__ __forceinline__ uint32_t block_key(const float* srow, int b, int nv, int I, int L) {
+// Selection key of block b with score v (v is not read for b >= nv).
+__device__ __forceinline__ uint32_t key_of(float v, int b, int nv, int I, int L) {
   if (b >= nv) return 0u;  // not a candidate (every finite score maps above 0)
   if (b < I || b >= nv - L) return kForcedKey;
-  return order_key(srow[b]);
+  return order_key(v);
+}
+
+__device__ __forceinline__ uint32_t block_key(const float* srow, int b, int nv, int I, int L) {
+  return key_of(b < nv ? srow[b] : 0.f, b, nv, I, L);
 }
 
 // Writes a selected id at its output slot and, with a sparse table, the
@@ -54,12 +59,13 @@ struct Emit {
   }
 };
 
-// E keys per lane in registers: rows with nv <= 64*E.
+// E keys per lane in registers: rows with nv <= 64*E.  raw[e] holds the
+// score of block 64e + lane, loaded before nv was known.
 template <int E, typename EmitT>
-__device__ void select_regs(const float* srow, int nv, const TopkArgs& a, EmitT& emit, int lane) {
+__device__ void select_regs(const float* raw, int nv, const TopkArgs& a, EmitT& emit, int lane) {
   uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = block_key(srow, 64 * e + lane, nv, a.init_blocks, a.local_blocks);
+  for (int e = 0; e < E; ++e) key[e] = key_of(raw[e], 64 * e + lane, nv, a.init_blocks, a.local_blocks);
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
@@ -116,12 +122,29 @@ __device__ void select_generic(const float* srow, int nv, const TopkArgs& a, Emi
 // SPARSE: also the row's sparse block table (one index head, page
 // "ops.index_topk", minimax_m3_index_decode: table construction fused into
 // the selector).
+// rows (waves) per workgroup; 8 and 16 measured equal or slower
+constexpr int kTopkWaves = 4;
+
 template <int E, bool SPARSE>
-__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * kTopkWaves + wave;
   const int h = blockIdx.y;
   if (t >= a.rows.tokens) return;
+  // The row's scores go out first: their address needs only the row, and
+  // their latency then overlaps that of the loads nv depends on (the
+  // request's length, or the row's block count).  Blocks past the score
+  // width are not read; blocks past nv are loaded but never used.
+  const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
+  constexpr int ER = E > 0 ? E : 1;
+  float raw[ER];
+  if constexpr (E > 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int b = 64 * e + lane;
+      raw[e] = b < a.s_width ? srow[b] : 0.f;
+    }
+  }
   int r = 0, pos = -1, nv;
   if (a.row_blocks != nullptr) {
     nv = a.row_blocks[t];  // given per row (never with a sparse table)
@@ -152,9 +175,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     }
     return;
   }
-  const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
-  if (E > 0)
-    select_regs<(E > 0 ? E : 1)>(srow, nv, a, emit, lane);
+  if constexpr (E > 0)
+    select_regs<ER>(raw, nv, a, emit, lane);
   else
     select_generic(srow, nv, a, emit, lane);
   if constexpr (SPARSE) {
@@ -169,7 +191,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 template <bool SPARSE>
 static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
   const int T = a.rows.tokens;
-  dim3 grid((T + 3) / 4, a.heads), block(256);
+  dim3 grid((T + kTopkWaves - 1) / kTopkWaves, a.heads), block(64 * kTopkWaves);
   const int nb = a.nb_max;
   if (nb <= 64)
     hipLaunchKernelGGL((topk_kernel<1, SPARSE>), grid, block, 0, s, a);
