@@ -125,39 +125,47 @@ __device__ void select_generic(const float* srow, int nv, const TopkArgs& a, Emi
 // rows (waves) per workgroup; 8 and 16 measured equal or slower
 constexpr int kTopkWaves = 4;
 
-template <int E, bool SPARSE>
-__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * kTopkWaves + wave;
-  const int h = blockIdx.y;
-  if (t >= a.rows.tokens) return;
-  // The row's scores go out first: their address needs only the row, and
-  // their latency then overlaps that of the loads nv depends on (the
-  // request's length, or the row's block count).  Blocks past the score
-  // width are not read; blocks past nv are loaded but never used.
-  const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
-  constexpr int ER = E > 0 ? E : 1;
-  float raw[ER];
-  if constexpr (E > 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int b = 64 * e + lane;
-      raw[e] = b < a.s_width ? srow[b] : 0.f;
-    }
-  }
-  int r = 0, pos = -1, nv;
+// Row t's request, position and visible-block count, and the end of its
+// request's rows.
+struct RowInfo {
+  int r, pos, nv, row_end;
+};
+
+__device__ __forceinline__ int blocks_at(int pos) { return pos < 0 ? 0 : pos / kBlock + 1; }
+
+__device__ __forceinline__ RowInfo row_info(const TopkArgs& a, int t) {
+  RowInfo ri{0, -1, 0, 0};
   if (a.row_blocks != nullptr) {
-    nv = a.row_blocks[t];  // given per row (never with a sparse table)
+    ri.nv = a.row_blocks[t];  // given per row (never with a sparse table)
   } else {
-    r = row_request(a.rows, t);
-    const ReqRows rr = req_rows(a.rows, r);
-    pos = rr.p0 + (t - rr.row0);
-    nv = pos < 0 ? 0 : pos / kBlock + 1;
+    ri.r = row_request(a.rows, t);
+    const ReqRows rr = req_rows(a.rows, ri.r);
+    ri.pos = rr.p0 + (t - rr.row0);
+    ri.nv = blocks_at(ri.pos);
+    ri.row_end = rr.row0 + rr.n;
   }
+  return ri;
+}
+
+// The scores of blocks 64e + lane of row t.  Columns past the score width
+// read the row's last column instead (every such block is past nv, so the
+// value is never used): no branch around the loads, which keeps the
+// compiler's wait counts exact when loads of the next row are in flight.
+template <int E>
+__device__ __forceinline__ void load_row(const TopkArgs& a, int h, int t, int lane, float* raw) {
+  const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
+#pragma unroll
+  for (int e = 0; e < E; ++e) raw[e] = srow[min(64 * e + lane, a.s_width - 1)];
+}
+
+template <int E, bool SPARSE>
+__device__ __forceinline__ void select_row(const TopkArgs& a, int h, int t, const RowInfo& ri,
+                                           const float* raw, int lane) {
+  const int nv = ri.nv, pos = ri.pos;
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)t * a.o_row;
   Emit<SPARSE> emit{orow, nullptr, nullptr, 0, 0, pos, 0};
   if constexpr (SPARSE) {
-    emit.abt = a.sp.abt + (int64_t)r * a.sp.abt_row;
+    emit.abt = a.sp.abt + (int64_t)ri.r * a.sp.abt_row;
     emit.st = a.sp.table + (int64_t)t * a.sp.st_row;
     emit.P = a.sp.pages_per_block;
     emit.stride = a.sp.block_page_stride;
@@ -175,10 +183,12 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
     }
     return;
   }
-  if constexpr (E > 0)
-    select_regs<ER>(raw, nv, a, emit, lane);
-  else
+  if constexpr (E > 0) {
+    select_regs<E>(raw, nv, a, emit, lane);
+  } else {
+    const float* srow = a.scores + (int64_t)h * a.s_head + (int64_t)t * a.s_row;
     select_generic(srow, nv, a, emit, lane);
+  }
   if constexpr (SPARSE) {
     // nv > topk: all topk slots hold ids, no padding
     int len = emit.len;
@@ -188,30 +198,90 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
   }
 }
 
-template <bool SPARSE>
+// One wave per run of RPW consecutive (head, row)s.  A row's scores go out
+// first: their address needs only the row, so their latency overlaps that of
+// the loads nv depends on (the request's length, or the row's block count).
+// With RPW > 1 the next row's scores (and block count, when given) are loaded
+// before the current row is selected, so a wave keeps them in flight while it
+// searches; the next row's position follows from the current one while both
+// rows are in one request, and is looked up only past its end.
+template <int E, bool SPARSE, int RPW, bool ROWB>
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
+  constexpr int ER = E > 0 ? E : 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  int t = (blockIdx.x * kTopkWaves + wave) * RPW;
+  if (t >= a.rows.tokens) return;
+  const int t_end = min(a.rows.tokens, t + RPW);
+  float raw[ER];
+  if constexpr (E > 0) load_row<E>(a, h, t, lane, raw);
+  RowInfo ri = row_info(a, t);
+  if constexpr (RPW == 1) {
+    select_row<E, SPARSE>(a, h, t, ri, raw, lane);
+  } else {
+    while (true) {
+      // the next row's loads (the last row reloads itself, unused)
+      const int tn = t + 1 < t_end ? t + 1 : t;
+      float raw_n[ER];
+      int nv_n = 0;
+      if constexpr (E > 0) load_row<E>(a, h, tn, lane, raw_n);
+      if constexpr (ROWB) nv_n = a.row_blocks[tn];
+      // keep these loads ahead of the selection's stores
+      asm volatile("" ::: "memory");
+      select_row<E, SPARSE>(a, h, t, ri, raw, lane);
+      if (tn == t) break;
+      for (int e = 0; e < ER; ++e) raw[e] = raw_n[e];
+      t = tn;
+      if constexpr (ROWB) {
+        ri.nv = nv_n;
+      } else if (t < ri.row_end) {
+        ri.pos += 1;
+        ri.nv = blocks_at(ri.pos);
+      } else {
+        ri = row_info(a, t);
+      }
+    }
+  }
+}
+
+#ifndef MM3_TOPK_RPW
+#define MM3_TOPK_RPW 4
+#endif
+
+template <bool SPARSE, int RPW, bool ROWB>
 static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
   const int T = a.rows.tokens;
-  dim3 grid((T + kTopkWaves - 1) / kTopkWaves, a.heads), block(64 * kTopkWaves);
+  const int waves = (T + RPW - 1) / RPW;
+  dim3 grid((waves + kTopkWaves - 1) / kTopkWaves, a.heads), block(64 * kTopkWaves);
   const int nb = a.nb_max;
   if (nb <= 64)
-    hipLaunchKernelGGL((topk_kernel<1, SPARSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<1, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
   else if (nb <= 128)
-    hipLaunchKernelGGL((topk_kernel<2, SPARSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<2, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
   else if (nb <= 256)
-    hipLaunchKernelGGL((topk_kernel<4, SPARSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<4, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
   else if (nb <= 512)
-    hipLaunchKernelGGL((topk_kernel<8, SPARSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<8, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
   else if (nb <= 1024)
-    hipLaunchKernelGGL((topk_kernel<16, SPARSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<16, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((topk_kernel<0, SPARSE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<0, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  // several rows per wave only when there are rows enough to keep every
+  // wave slot of the chip busy that way (prefill-sized batches)
+  const int64_t rows = (int64_t)a.rows.tokens * a.heads;
+  const bool multi = MM3_TOPK_RPW > 1 && rows >= 65536 && a.nb_max <= 1024;
+  const bool rowb = a.row_blocks != nullptr;
   if (a.sparse)
-    launch_topk_t<true>(a, s);
+    launch_topk_t<true, 1, false>(a, s);
+  else if (multi && rowb)
+    launch_topk_t<false, MM3_TOPK_RPW, true>(a, s);
+  else if (multi)
+    launch_topk_t<false, MM3_TOPK_RPW, false>(a, s);
   else
-    launch_topk_t<false>(a, s);
+    launch_topk_t<false, 1, false>(a, s);
   return hipGetLastError();
 }
 

@@ -696,3 +696,37 @@ def test_scores_past_2gib_use_direct_stores():
     assert torch.equal(out, o_ref)
     del buf, big
     torch.cuda.empty_cache()
+
+
+def test_selector_many_rows_ragged():
+    """Above 65536 (row, head) pairs the selector runs several rows per wave
+    and carries a row's position over from the previous one within a
+    request.  Ragged requests of odd lengths (runs of rows cross request
+    boundaries, empty requests) against the oracle's selection on the same
+    GPU scores: ids equal exactly."""
+    import oracle
+    w = make(name="many_rows", R=9, lens=(0, 0), Q=5000, H=4, max_seq_len=8192, topk=16, I=1,
+             L=2, kfmt=KFMT_BF16, seed=81, device=DEV,
+             fixed_lens=[8000, 3000, 5, 700, 8150, 6000, 7, 0, 7000],
+             qlens=[4999, 3, 1, 0, 5000, 2001, 7, 0, 4444], prefix="gap")
+    assert w.rows * w.heads >= 65536
+    scores, out = run_split(w)
+    s = scores.cpu().numpy()
+    ids_ref = oracle.topk(s, w.seq_lens.cpu().numpy(), w.query_len, w.topk, w.init_blocks,
+                          w.local_blocks, cu_seqlens_q=_np(w.cu_seqlens_q),
+                          prefix_lens=_np(w.prefix_lens))
+    assert np.array_equal(out.cpu().numpy(), ids_ref)
+    invariants(w, out)
+
+
+def test_topk_blocks_many_rows():
+    H, T, nb = 4, 20000, 100
+    g = torch.Generator(device=DEV).manual_seed(82)
+    W = 112
+    s = torch.randint(-40, 40, (H, T, W), generator=g, device=DEV).float() * 0.25
+    nv = torch.randint(0, nb + 1, (T,), generator=g, device=DEV).to(torch.int32)
+    out = torch.full((H, T, 16), -7, dtype=torch.int32, device=DEV)
+    mm3.mm3_index_topk_blocks(s, nv, 128 * nb, 16, 1, 2, out=out)
+    torch.cuda.synchronize()
+    want = _oracle_by_blocks(s.cpu().numpy(), nv.cpu().numpy(), 16, 1, 2)
+    assert np.array_equal(out.cpu().numpy(), want)
