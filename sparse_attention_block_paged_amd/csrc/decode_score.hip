@@ -27,6 +27,8 @@
 // only, so they are fixed under graph capture.  Unlike the pages' Triton
 // split-K kernel there is no per-chunk partial result: a block's score is
 // complete inside one wave, so the split needs no merge.
+#include <atomic>
+
 #include "mm3_device.h"
 #include "mm3_fp4.h"
 #include "mm3_launch.h"
@@ -595,16 +597,18 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
 // Largest batch whose lengths and prefix sums fit the per-CU scorer's LDS.
 constexpr int kCuMaxReqs = 4096;
 
+// Compute units of the current device, cached per device (host threads may
+// race on the first call; they store the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  int n = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <int KFMT>

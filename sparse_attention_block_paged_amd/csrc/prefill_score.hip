@@ -33,6 +33,8 @@
 //     scatter over 64 rows per instruction).
 // Two workgroups (80 KiB of LDS each) share a CU, so one's barrier or copy
 // wait is covered by the other's multiplies.
+#include <atomic>
+
 #include "mm3_device.h"
 #include "mm3_fp4.h"
 #include "mm3_launch.h"
@@ -458,20 +460,23 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
   }
 }
 
+// Persistent grid: workgroups that fit the chip at once, cached per device.
 template <int KFMT>
 static int prefill_grid() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cache[dev]) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int g = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (g <= 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_score_kernel<KFMT, true>, kPfThreads, 0) !=
             hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
-    cache[dev] = device_cus() * per_cu;
+    g = device_cus() * per_cu;
+    if (dev < 64) cache[dev].store(g, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return g;
 }
 
 template <int KFMT>
