@@ -533,6 +533,7 @@ def cpu_baseline(w, seq, seconds, pool=None, cores=0):
                    f"64 rows; longer ones in passes of 16 rows), {int(tok)} tokens-equivalent, "
                    f"{el:.1f} s, single-threaded fp64 C oracle"),
         "host_cpus": os.cpu_count(),
+        "host_cpu_model": host_cpu_model(),
     }
     if pool is not None:
         try:
@@ -540,6 +541,18 @@ def cpu_baseline(w, seq, seconds, pool=None, cores=0):
         except Exception as e:  # the single-threaded figure stands on its own
             res["all_cores"] = {"error": f"{type(e).__name__}: {e}"}
     return res
+
+
+def host_cpu_model() -> str:
+    """The host processor's model name, from /proc/cpuinfo ("" where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 if __name__ == "__main__":
