@@ -396,22 +396,39 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
   };
 
   // write staged columns [0, nst) = blocks bfirst.. of the wave's rows; only
-  // visible (row, block) entries are written
+  // visible (row, block) entries are written.  Lane l takes column l % 8 of
+  // rows l / 8 + 8k, k = 0..15.  Eight rows further on, a row's position,
+  // head and score offset move by fixed amounts (one carry when the head
+  // wraps), so the loop needs no division and no 64-bit multiply.
   auto flush = [&](int bfirst, int nst) __attribute__((always_inline)) {
-    const int c = lane & 7;
+    const int c = lane & 7, rl = lane >> 3;
     const int b = bfirst + c;
     const int HQ = H * cur.n;
-    // not unrolled: unrolled, the compiler keeps every row's address live
-    // through the whole loop and spills
-#pragma unroll 1
+    const int i0 = cur.x * kPrefillRows + kPfWaveRows * wave + rl;
+    int j = i0 / H, h = i0 - j * H;         // row i0: position p0 + j, head h
+    const int dj = 8 / H, dh = 8 - dj * H;  // the step of 8 rows
+    int64_t off = (int64_t)h * a.s_head + (int64_t)(cur.row0 + j) * a.s_row + b;
+    const int64_t doff = (int64_t)dh * a.s_head + (int64_t)dj * a.s_row;
+    const int64_t wrap = a.s_row - (int64_t)H * a.s_head;
+    const float* sv = stage + rl * kPfStage + (c ^ rl);  // row rl + 8k at + 64k
+    const bool col_ok = c < nst;
+    // all reads first: left next to their stores, each would wait out the
+    // LDS latency inside its own branch
+    float v[kPfWaveRows / 8];
+#pragma unroll
+    for (int k = 0; k < kPfWaveRows / 8; ++k) v[k] = sv[8 * kPfStage * k];
+#pragma unroll
+    for (int k = 0; k < kPfWaveRows / 8; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
     for (int k = 0; k < kPfWaveRows / 8; ++k) {
-      const int rho = 8 * k + (lane >> 3);
-      const int i = cur.x * kPrefillRows + kPfWaveRows * wave + rho;
-      if (c < nst && i < HQ) {
-        const int j = i / H, h = i - j * H;
-        if (cur.p0 + j >= kBlock * b)
-          a.scores[(int64_t)h * a.s_head + (int64_t)(cur.row0 + j) * a.s_row + b] =
-              stage[rho * kPfStage + (c ^ (rho & 7))];
+      if (col_ok && i0 + 8 * k < HQ && cur.p0 + j >= kBlock * b) a.scores[off] = v[k];
+      j += dj;
+      h += dh;
+      off += doff;
+      if (h >= H) {
+        h -= H;
+        ++j;
+        off += wrap;
       }
     }
   };
