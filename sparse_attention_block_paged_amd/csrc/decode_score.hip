@@ -379,8 +379,8 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut,
       __builtin_amdgcn_sched_barrier(0);
       issue_half<KFMT>(rb.h1, a, nxt.page, 1, n, g, has_next);
       __builtin_amdgcn_sched_barrier(0);
-      m = wave_max_xor(m, 16);
-      m = wave_max_xor(m, 32);
+      m = wave_max_xor16(m);
+      m = wave_max_xor32(m);
       const bool writer = n < HQ && q.pos >= kBlock * cur.b;
       const int64_t off = (int64_t)q.h * a.s_head + (int64_t)q.t * a.s_row + cur.b;
       if constexpr (STAGED) {

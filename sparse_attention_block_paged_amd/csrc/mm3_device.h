@@ -52,8 +52,19 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Key of a forced (init / local) block: above every finite score.
 constexpr uint32_t kForcedKey = 0xFFFFFFFFu;
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, kWave));
+// max(v, v of lane l ^ 16) and max(v, v of lane l ^ 32), without an LDS
+// round trip.  The gfx950 lane-swap instructions exchange the odd 16-lane
+// rows of one copy of v with the even rows of another (permlane16_swap), or
+// the upper 32 lanes of one with the lower 32 of the other (permlane32_swap);
+// afterwards each lane holds its own value in one copy and its partner's in
+// the other, so the max of the two copies is the pairwise max.
+__device__ __forceinline__ float wave_max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 }  // namespace mm3

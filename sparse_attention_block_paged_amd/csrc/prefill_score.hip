@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) m[qt] = wave_max_xor(m[qt], 32);
+    for (int qt = 0; qt < 4; ++qt) m[qt] = wave_max_xor32(m[qt]);
     // lane (nl, kg) stages rows 64kg + nl and 64kg + 32 + nl (tiles 2kg, 2kg+1)
     const int r0 = 64 * kg + nl, r1 = r0 + 32;
     stage[r0 * kPfStage + (col ^ (r0 & 7))] = (kg ? m[2] : m[0]) * a.sm_scale;
