@@ -43,9 +43,17 @@
 namespace mm3 {
 
 constexpr int kPageBytes = kBlock * kDim * 2;              // 32 KiB
-constexpr int kPfWaves = 4;                                  // waves per workgroup
-constexpr int kPfWaveRows = 128;                             // query rows per wave
-static_assert(kPfWaves * kPfWaveRows == kPrefillRows, "row tile");
+// Four waves of 128 rows, two workgroups per CU.  Eight waves of 64 rows (one
+// workgroup per CU, its waves in step at every block) read each key fragment
+// for two multiplies instead of four and measured 3-7% slower.
+#ifndef MM3_PF_WAVES
+#define MM3_PF_WAVES 4
+#endif
+constexpr int kPfWaves = MM3_PF_WAVES;                       // waves per workgroup
+constexpr int kPfWaveRows = kPrefillRows / kPfWaves;         // query rows per wave
+constexpr int kPfQt = kPfWaveRows / 32;                      // 32-row MFMA B tiles per wave
+constexpr int kPfWgPerCu = 8 / kPfWaves;                     // two waves per SIMD
+static_assert(kPfWaves == 4 || kPfWaves == 8, "row tile");
 constexpr int kPfStage = 8;                                  // blocks staged per write-out
 #ifndef MM3_PF_AHEAD
 #define MM3_PF_AHEAD 3
@@ -135,7 +143,7 @@ struct PfCursor {
 };
 
 template <int KFMT, bool BALANCED>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs a, int units, int tiles) {
+__global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(ScoreArgs a, int units, int tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLdsOf<KFMT>];
   // bf16: two page buffers.  NVFP4: one decoded page buffer plus two staging
   // slots for the raw page.
@@ -239,15 +247,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
 
   // ---- this wave's query rows of the current tile
   const int nl = lane & 31, kg = lane >> 5;
-  bf16x8 qb[4][8];
-  int pos_q[4];
+  bf16x8 qb[kPfQt][8];
+  int pos_q[kPfQt];
   int wave_pos_min = 0, wave_pos_max = -1;
   bool wave_live = false;
   auto load_q = [&]() __attribute__((always_inline)) {
     const int HQ = H * cur.n;  // >= 1: the unit has steps
     const int wrow0 = cur.x * kPrefillRows + kPfWaveRows * wave;
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
+    for (int qt = 0; qt < kPfQt; ++qt) {
       const int i = wrow0 + 32 * qt + nl;
       const bool ok = i < HQ;
       const int ic = ok ? i : HQ - 1;
@@ -279,34 +287,39 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     wait_vmcnt<0>();
   };
 
-  // ---- page copies.  Copy k of wave w fills LDS bytes [(4k + w) KiB, +1 KiB):
-  // lane l the 16-byte slot of token t = 16k + t0 (t0 = 4w + l/16) at slot
-  // l%16, which holds chunk (l%16) ^ (t & 15) of the token (t & 15 == t0).
+  // ---- page copies.  One copy instruction of a wave moves 1 KiB (4 tokens);
+  // a round of all the workgroup's waves moves kCopyRound bytes.  Copy k of
+  // wave w fills LDS bytes [k kCopyRound + w KiB, +1 KiB): lane l the 16-byte
+  // slot of token t = 4 kPfWaves k + t0 (t0 = 4w + l/16) at slot l%16, which
+  // holds chunk (l%16) ^ (t & 15) of the token (t & 15 == t0 & 15).
+  constexpr int kCopyRound = 1024 * kPfWaves;
   const int t0 = 4 * wave + (lane >> 4);
-  const uint32_t src0 = t0 * (kDim * 2) + (((lane & 15) ^ t0) << 4);
+  const uint32_t src0 = t0 * (kDim * 2) + (((lane & 15) ^ (t0 & 15)) << 4);
   auto copy_page = [&](uint8_t* kl, const PfCursor& c) __attribute__((always_inline)) {
     const uint8_t* pg = a.kdata + (int64_t)bt_s[(int64_t)c.r * a.bt_stride + c.b] * kPageBytes;
     const uint32_t l0 = (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)kl + 1024 * wave;
-    // the 4 KiB steps go on the scalar base: one offset register for all
+    // the round steps go on the scalar base: one offset register for all
 #pragma unroll
-    for (int k = 0; k < kPfCopies; ++k) copy16_to_lds(l0 + 4096 * k, pg + 4096 * k, src0);
+    for (int k = 0; k < kPfCopies; ++k) copy16_to_lds(l0 + kCopyRound * k, pg + kCopyRound * k, src0);
   };
 
-  // NVFP4: copy k (0, 1) of wave w moves nibble KiB 4k + w of the page, and
-  // wave 0 also moves the 1 KiB of scales, into staging slot `slot`.
+  // NVFP4: copy k of wave w moves nibble KiB kPfWaves k + w of the page (the
+  // 8 KiB in 8 / kPfWaves rounds), and wave 0 also moves the 1 KiB of scales,
+  // into staging slot `slot`.
   auto copy_fp4 = [&](int slot, const PfCursor& c) __attribute__((always_inline)) {
     const int64_t page = bt_s[(int64_t)c.r * a.bt_stride + c.b];
     const uint8_t* nib = a.kdata + page * kFp4NibBytes;
     const uint32_t l0 =
         (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Stage0 + slot * kFp4NibBytes) + 1024 * wave;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) copy16_to_lds(l0 + 4096 * k, nib + 4096 * k + 1024 * wave, 16 * lane);
+    for (int k = 0; k < kFp4NibBytes / kCopyRound; ++k)
+      copy16_to_lds(l0 + kCopyRound * k, nib + kCopyRound * k + 1024 * wave, 16 * lane);
     if (wave == 0)
       copy16_to_lds((uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Scale0 + slot * kFp4ScaleBytes),
                     a.kscales + page * kFp4ScaleBytes, 16 * lane);
   };
   // decode staging slot `slot` into kbuf0: thread t handles the 16-byte
-  // chunks t + 256j (token q/16, chunk q%16 = dims 8(q%16)..+8)
+  // chunks q = t + kPfThreads j (token q/16, chunk q%16 = dims 8(q%16)..+8)
   auto decode_fp4 = [&](int slot) __attribute__((always_inline)) {
     const uint8_t* nib = smem + kPfFp4Stage0 + slot * kFp4NibBytes;
     const uint8_t* scl = smem + kPfFp4Scale0 + slot * kFp4ScaleBytes;
@@ -328,7 +341,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     if (!(wave_live && wave_pos_max >= kBlock * b)) return;
     // every row of the wave sees the whole block
     const bool full = kBlock * b + (kBlock - 1) <= wave_pos_min;
-    float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float m[kPfQt];
+#pragma unroll
+    for (int qt = 0; qt < kPfQt; ++qt) m[qt] = -INFINITY;
     // Key fragment of step st: tokens 32(st/8) + nl, 16-byte chunk
     // 2(st%8) + kg, at swz().  With tok & 15 == nl & 15 == 2p + e, the chunk
     // slot (2kk + kg) ^ (2p + e) is 2(kk ^ p) + (kg ^ e), so the address is
@@ -355,24 +370,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
     bf16x8 fr[kPfAhead + 1];
 #pragma unroll
     for (int p = 0; p < kPfAhead; ++p) fr[p] = frag(p);
-    f32x16 acc[4];
+    f32x16 acc[kPfQt];
 #pragma unroll
     for (int st = 0; st < 32; ++st) {
       const int tt = st >> 3, kk = st & 7;
       if (st + kPfAhead < 32) fr[(st + kPfAhead) % (kPfAhead + 1)] = frag(st + kPfAhead);
-      if (kk == 0) acc[0] = acc[1] = acc[2] = acc[3] = f32x16{};
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) acc[qt] = mfma32(fr[st % (kPfAhead + 1)], qb[qt][kk], acc[qt]);
+      for (int qt = 0; qt < kPfQt; ++qt) {
+        if (kk == 0) acc[qt] = f32x16{};
+        acc[qt] = mfma32(fr[st % (kPfAhead + 1)], qb[qt][kk], acc[qt]);
+      }
       if (kk == 7) {
         // acc[qt][i]: token 32tt + 8(i/4) + 4kg + i%4 against row nl of tile qt
         if (full) {
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt)
+          for (int qt = 0; qt < kPfQt; ++qt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) m[qt] = fmaxf(m[qt], acc[qt][i]);
         } else {
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) {
+          for (int qt = 0; qt < kPfQt; ++qt) {
             // visible iff 8(i/4) + i%4 <= pos - 128b - 32tt - 4kg
             const int d = pos_q[qt] - kBlock * b - 32 * tt - 4 * kg;
 #pragma unroll
@@ -388,11 +405,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) m[qt] = wave_max_xor32(m[qt]);
-    // lane (nl, kg) stages rows 64kg + nl and 64kg + 32 + nl (tiles 2kg, 2kg+1)
-    const int r0 = 64 * kg + nl, r1 = r0 + 32;
-    stage[r0 * kPfStage + (col ^ (r0 & 7))] = (kg ? m[2] : m[0]) * a.sm_scale;
-    stage[r1 * kPfStage + (col ^ (r1 & 7))] = (kg ? m[3] : m[1]) * a.sm_scale;
+    for (int qt = 0; qt < kPfQt; ++qt) m[qt] = wave_max_xor32(m[qt]);
+    // both lane halves now hold every tile's row maxima: lane (nl, kg) stages
+    // row 32 qt + nl of tiles qt = kPfQt/2 kg .. kPfQt/2 kg + kPfQt/2 - 1
+#pragma unroll
+    for (int u = 0; u < kPfQt / 2; ++u) {
+      const int qt = (kPfQt / 2) * kg + u, r = 32 * qt + nl;
+      stage[r * kPfStage + (col ^ (r & 7))] = (kg ? m[kPfQt / 2 + u] : m[u]) * a.sm_scale;
+    }
   };
 
   // write staged columns [0, nst) = blocks bfirst.. of the wave's rows; only
@@ -435,7 +455,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_score_kernel(ScoreArgs 
 
   // ---- the ring: block of step i sits in buffer i & 1; the copy of step
   // i + 1 is started once every wave is past step i - 1.
-  if constexpr (KFMT == 1) fill_lut(lut);  // read after the first ring barrier
+  if constexpr (KFMT == 1) {
+    if (threadIdx.x < 256) fill_lut(lut);  // read after the first ring barrier
+  }
   load_q();
   PfCursor nxt = cur;
   if constexpr (KFMT == 0)
