@@ -379,11 +379,25 @@ def summarize_rocprof(d, label, record):
     pmc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if stats:
         rows = _read_csv(stats[0])
+        # medians from the dispatch trace: the averages include the first,
+        # cold launches (page pool first touched, caches empty)
+        med = {}
+        trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+        if trace:
+            durs = {}
+            for r in _read_csv(trace[0]):
+                ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                durs.setdefault(r["Kernel_Name"], []).append(ns)
+            for name, v in durs.items():
+                v.sort()
+                med[name] = v[len(v) // 2]
         print(f"# kernel statistics ({label})")
-        print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total%':>7s}")
+        print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'med_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+              f"{'total%':>7s}")
         for r in rows[:12]:
             name = r.get("Name", r.get("KernelName", "?"))
-            print(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
+            m = f"{med[name] / 1e3:10.2f}" if name in med else f"{'-':>10s}"
+            print(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} {m} "
                   f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} {float(r['Percentage']):7.2f}")
     if pmc:
         rows = _read_csv(pmc[0])
