@@ -129,8 +129,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the indexer on one GPU; --gpus above 1 is not "
-              "supported (requests shard across GPUs with no exchange; see the design notes)",
+        print("bench.py: the indexer runs on one GPU; --gpus above 1 is not supported "
+              "(requests would shard across GPUs with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -477,7 +477,7 @@ def _oracle_init():
 
 
 def cpu_baseline_all_cores(tasks, pool, cores):
-    """The same oracle tasks on every host core the box gives this job (16 at
+    """The same oracle tasks on the host cores this process may use (16 at
     most), one task at a time per worker process; the workers never touch the
     GPU.  The time is the busiest worker's time inside the oracle: shipping a
     request's pages to a worker process is not the oracle's work (the

@@ -21,8 +21,7 @@
  * final sm_scale * max is rounded once to the fp32 score the pages' score
  * tensors hold (torch.float32 in minimax_m3_index_decode / _new_score).
  *
- * Readings taken where the pages are silent (each is listed with its reason
- * in the repository's design notes):
+ * Readings taken where the pages are silent:
  *   - the Q rows of request r sit at positions seq_len[r]-Q+j, j<Q;
  *   - ragged batches (minimax_m3_index_score / minimax_m3_index_topk take
  *     cu_seqlens_q and prefix_lens): request r owns rows

@@ -17,9 +17,10 @@
 //     start), so the chip stays full to the end whatever the causal triangle
 //     and the length mix look like.  Every (row, block) score is produced by
 //     exactly one step: shares need no merge.
-//   * Wave w owns rows 128w..128w+127 of the tile as four 32-row MFMA B tiles
-//     held in registers (loaded again only when the share crosses into the
-//     next tile); each key fragment read from LDS feeds four MFMAs.
+//   * Wave w owns rows 128w..128w+127 of the tile (with the default four
+//     waves) as four 32-row MFMA B tiles held in registers (loaded again only
+//     when the share crosses into the next tile); each key fragment read from
+//     LDS feeds four MFMAs.
 //   * Key pages (32 KiB) go global -> LDS by direct DMA (no registers), double
 //     buffered one block ahead, with a 16-byte-chunk XOR swizzle (chunk c of
 //     token s at c ^ (s & 15)) so the A-operand reads of 32 tokens x 16 B are
