@@ -239,6 +239,15 @@ int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStr
   return e == hipSuccess ? MM3_OK : hip_fail(e, "scorer launch");
 }
 
+// Bytes from a score tensor's base to one past its last element, or 0 when
+// that is 2^31 - 64 or more (kernels that address it through one buffer
+// descriptor then take another path).
+int32_t score_bytes(int64_t sh, int64_t sr, int64_t sw, int64_t heads, int64_t T) {
+  if (T == 0) return 0;
+  const int64_t extent = ((heads - 1) * sh + (T - 1) * sr + sw) * 4;
+  return extent > 0 && extent <= 0x7FFFFFC0 ? (int32_t)extent : 0;
+}
+
 TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t sw, int32_t heads,
                    const mm3_rows* rows, int32_t topk, int32_t I, int32_t L, int32_t* out, int64_t oh,
                    int64_t orow) {
@@ -256,6 +265,7 @@ TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t sw, int32_t h
   a.init_blocks = I;
   a.local_blocks = L;
   a.nb_max = (int32_t)cdiv64(rows->max_seq_len, MM3_BLOCK);
+  a.s_bytes = score_bytes(sh, sr, sw, heads, rows->total_q);
   return a;
 }
 
@@ -345,6 +355,7 @@ int mm3_index_topk_blocks(const float* scores, int64_t s_head_stride, int64_t s_
   a.local_blocks = local_blocks;
   a.nb_max = (int32_t)nb;
   a.row_blocks = row_blocks;
+  a.s_bytes = score_bytes(s_head_stride, s_row_stride, s_width, heads, T);
   hipError_t e = launch_topk(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();

@@ -77,6 +77,8 @@ struct TopkArgs {
   SparseOut sp;   // used when sparse != 0 (heads == 1)
   int32_t sparse;
   const int32_t* row_blocks;  // when set: nv per row, instead of rows' positions
+  int32_t s_bytes;            // bytes from scores to one past its last element
+                              // (0 when that exceeds 2^31 - 64)
 };
 
 struct SparseTableArgs {

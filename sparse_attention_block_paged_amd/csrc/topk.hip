@@ -244,8 +244,293 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
   }
 }
 
+// ---- one lane per row
+//
+// For batches with many short rows (prefill chunks), each lane selects one
+// (head, row) pair by itself.  The selection then runs on the vector units,
+// 64 rows per instruction, instead of as the per-row ballot search above,
+// whose scalar popcounts, compares and branches all queue on the CU's one
+// scalar unit (about 8 scalar instructions per search step, ~15 steps per
+// row).  The wave reads its 64 rows in chunks of 16 blocks with coalesced
+// loads (64 contiguous bytes per row and chunk) and hands each lane its
+// row's chunk through LDS.  A lane keeps its whole row's keys (at most
+// 16*NC blocks) in registers, and the 16 largest of them sorted:
+//   * each chunk of 16 keys is sorted by a bitonic network;
+//   * the elementwise max of the kept list (descending) and the reversed
+//     chunk holds the 16 largest of both, as a bitonic sequence;
+//   * a half-cleaner cascade sorts it again.
+// The topk-th kept key is the threshold T.  A second pass over the registers
+// takes the blocks above T, and those equal to T in ascending id order until
+// topk are chosen: the same set as the ballot search, written in the same
+// ascending order.
+constexpr int kLaneTop = 16;  // kept keys per lane: topk <= 16
+
+__device__ __forceinline__ void cx_desc(uint32_t& hi, uint32_t& lo) {
+  const uint32_t m = max(hi, lo);
+  lo = min(hi, lo);
+  hi = m;
+}
+
+// 16 keys into descending order.
+__device__ __forceinline__ void sort16_desc(uint32_t (&x)[16]) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          // runs with bit k clear descend, the others ascend; the last
+          // stage (k = 16) leaves one descending run
+          if ((i & k) == 0)
+            cx_desc(x[i], x[l]);
+          else
+            cx_desc(x[l], x[i]);
+        }
+      }
+}
+
+// top (descending) := the 16 largest of top and x (both descending).
+__device__ __forceinline__ void merge16_desc(uint32_t (&top)[16], const uint32_t (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) top[i] = max(top[i], x[15 - i]);
+#pragma unroll
+  for (int j = 8; j > 0; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & j) == 0) cx_desc(top[i], top[i + j]);
+}
+
+// The last request in [lo, hi] whose first row is <= t (ragged batches;
+// cu[lo] <= t).
+__device__ __forceinline__ int lane_request(const Rows& m, int t, int lo, int hi) {
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (m.cu[mid] <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// The selection key of key_of, without branches or per-block compares
+// (compare results are 64-bit scalar masks, and a chunk's worth of them
+// spills).  Per chunk of 16 blocks a lane makes two 16-bit masks, of its
+// visible and of its forced blocks; block i of the chunk takes its bits by
+// a sign-extending bit-field extract (0 or all ones).  Adding +0 turns -0
+// into +0 and leaves every other finite value as it is.
+__device__ __forceinline__ uint32_t chunk_key(float v, int i, uint32_t vism, uint32_t fm) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // order_key
+  return (k | (uint32_t)__builtin_amdgcn_sbfe((int)fm, i, 1)) & (uint32_t)__builtin_amdgcn_sbfe((int)vism, i, 1);
+}
+
+// Bits [0, min(max(n, 0), 16)) of a 16-bit mask.
+__device__ __forceinline__ uint32_t low_bits16(int n) { return (1u << min(max(n, 0), 16)) - 1u; }
+
+// (k > thr, k == thr) as 0/1, each compare's mask used by the next
+// instruction (the compiler would gather a run of compares first).
+__device__ __forceinline__ void cmp_bits(uint32_t k, uint32_t thr, uint32_t& gt, uint32_t& eq) {
+  asm("v_cmp_gt_u32 vcc, %2, %3\n\t"
+      "v_cndmask_b32 %0, 0, 1, vcc\n\t"
+      "v_cmp_eq_u32 vcc, %2, %3\n\t"
+      "v_cndmask_b32 %1, 0, 1, vcc"
+      : "=&v"(gt), "=&v"(eq)
+      : "v"(k), "v"(thr)
+      : "vcc");
+}
+
+// Per-wave LDS row of one chunk (16 scores), padded so that both the
+// chunk's writes (16 rows x 64 bytes per instruction) and the lanes' row
+// reads spread over the banks.
+constexpr int kLaneRowFloats = 20;
+// Chunks whose loads a wave keeps in flight ahead of the one it sorts.
+#ifndef MM3_LANE_AHEAD
+#define MM3_LANE_AHEAD 2
+#endif
+constexpr int kLaneAhead = MM3_LANE_AHEAD;
+
+// One chunk (16 blocks) of the wave's 64 rows with coalesced loads: load q
+// takes rows 16q + l/4 (l = lane), 16 bytes each at column 4*(l%4) of the
+// chunk, so each instruction reads 16 runs of 64 contiguous bytes.
+__device__ __forceinline__ void lane_chunk_load(f32x4 (&g)[4], const __amdgpu_buffer_rsrc_t& rs,
+                                                const int (&roff)[4], int c) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    g[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, roff[q], 64 * c, 0));
+}
+
+// Rows of 16*NC blocks at most; the score rows are 16-byte aligned and the
+// tensor spans s_bytes < 2 GiB (checked by the launcher).
+template <int NC, bool ROWB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void topk_lanes_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) float tr[4][64 * kLaneRowFloats];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const int t0 = (blockIdx.x * 4 + wave) * 64;  // the wave's first row
+  if (t0 >= a.rows.tokens) return;
+  const int T = a.rows.tokens;
+  const int t = t0 + lane;
+  const bool live = t < T;
+  const int tc = live ? t : T - 1;
+  // The loads nv depends on go out first.  Memory loads retire in issue
+  // order, so nv's wait then leaves the first chunks' score loads in
+  // flight.  (A ragged batch's request search, whose loads depend on each
+  // other, completes before them.)  Raw values only, no arithmetic on them
+  // yet, which would wait: row t of request r sits at seq_lens[r] - c1 + t
+  // (c1 = the request's end row), or at prefix[r] + t - c0 (c0 = its first
+  // row) with prefix lengths.
+  int nv_raw = 0, base = 0, c0 = 0, c1 = 0;
+  const Rows& m = a.rows;
+  if constexpr (ROWB) {
+    nv_raw = a.row_blocks[tc];
+  } else if (m.cu == nullptr) {
+    const int r = tc / m.qlen;
+    c1 = (r + 1) * m.qlen;
+    base = m.seq_lens[r];
+  } else {
+    // the wave's rows lie in requests [r_lo, r_hi]
+    const int r_lo = row_request(m, t0);
+    const int r_hi = row_request(m, min(t0 + 63, T - 1));
+    const int r = lane_request(m, tc, r_lo, r_hi);
+    c0 = m.cu[r];
+    c1 = m.cu[r + 1];
+    base = m.prefix != nullptr ? m.prefix[r] : m.seq_lens[r];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // The scores, one chunk ahead.  One buffer descriptor spans the score
+  // tensor (under 2 GiB, checked by the launcher); rows past the batch read
+  // its last row, and columns past a row's width read the next row (or
+  // zeros past the tensor's end): all of them belong to blocks >= nv, whose
+  // values are not used.
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.scores, (short)0, a.s_bytes, 0x00020000);
+  int roff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tq = min(t0 + 16 * q + lane / 4, T - 1);
+    roff[q] = (int)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) + 16 * (lane % 4);
+  }
+  constexpr int PD = NC < kLaneAhead ? NC : kLaneAhead;  // chunks in flight
+  f32x4 g[PD][4];
+#pragma unroll
+  for (int c = 0; c < PD; ++c) lane_chunk_load(g[c], rs, roff, c);
+  __builtin_amdgcn_sched_barrier(0);
+  int nv = 0;
+  if constexpr (ROWB)
+    nv = live ? nv_raw : 0;
+  else
+    nv = live ? blocks_at(m.prefix != nullptr ? base + tc - c0 : base - c1 + tc) : 0;
+  const int I = a.init_blocks, L = a.local_blocks;
+  // the row's keys, in place of its scores (both passes read them), made
+  // chunk by chunk: a chunk's sort waits only for its own loads
+  uint32_t kk[16 * NC];
+  uint32_t top[kLaneTop];
+  float* trw = tr[wave];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    // chunk c through the wave's LDS rows: written as loaded, read back one
+    // row per lane; chunk c + PD's loads go out in between.  (The fences
+    // keep the compiler from moving LDS accesses across the exchange, as it
+    // sees only each lane's own addresses; one wave's LDS accesses execute
+    // in order.)
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(trw + (16 * q + lane / 4) * kLaneRowFloats + 4 * (lane % 4)) = g[c % PD][q];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (c + PD < NC) lane_chunk_load(g[c % PD], rs, roff, c + PD);
+    f32x4 rv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rv[j] = *reinterpret_cast<const f32x4*>(trw + lane * kLaneRowFloats + 4 * j);
+    // this chunk's visible blocks [16c, nv) and forced ones [16c, I) and
+    // [nv - L, nv), as bits of the chunk
+    const uint32_t vism = low_bits16(nv - 16 * c);
+    const uint32_t fm = low_bits16(I - 16 * c) | (vism & ~low_bits16(nv - L - 16 * c));
+    uint32_t x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      kk[16 * c + i] = chunk_key(rv[i / 4][i % 4], i, vism, fm);
+      x[i] = kk[16 * c + i];
+    }
+    sort16_desc(x);
+    if (c == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) top[i] = x[i];
+    } else {
+      merge16_desc(top, x);
+    }
+    // the next chunk's exchange stays after this chunk's sort, so the loads
+    // in flight have the sort's time to arrive
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int K = a.topk;
+  uint32_t thr = top[0];
+#pragma unroll
+  for (int j = 1; j < kLaneTop; ++j)
+    if (j < K) thr = top[j];
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < kLaneTop; ++j) gt += (j < K && top[j] > thr) ? 1 : 0;
+  const int need = K - gt;
+  // The selection as a bitmask (bit b of word b/32), then the ids in
+  // ascending order from it: no branch or store inside the block loop.
+  // Blocks above T, and of those equal to T the first `need` by id.  Blocks
+  // past nv have key 0 and every visible block a key above 0, so a
+  // threshold of 0 (fewer than topk visible) takes no ties.
+  constexpr int NW = NC / 2;
+  uint32_t selm[NW], eqm[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) selm[w] = eqm[w] = 0u;
+#pragma unroll
+  for (int b = 0; b < 16 * NC; ++b) {
+    uint32_t gtb, eqb;
+    cmp_bits(kk[b], thr, gtb, eqb);
+    selm[b / 32] |= gtb << (b % 32);
+    eqm[b / 32] |= eqb << (b % 32);
+  }
+  int left = thr != 0u ? need : 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    uint32_t x = eqm[w], keep = 0u;
+    const int n = __popc(x);
+    if (left >= n) {
+      keep = x;
+      left -= n;
+    } else {
+      for (int j = 0; j < left; ++j) {
+        const uint32_t lb = x & (0u - x);
+        keep |= lb;
+        x ^= lb;
+      }
+      left = 0;
+    }
+    selm[w] |= keep;
+  }
+  if (!live) return;
+  int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)tc * a.o_row;
+  for (int j = 0; j < K; ++j) {
+    int id = -1;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (!found && selm[w] != 0u) {
+        id = 32 * w + __builtin_ctz(selm[w]);
+        selm[w] &= selm[w] - 1u;
+        found = true;
+      }
+    }
+    orow[j] = id;
+  }
+}
+
 #ifndef MM3_TOPK_RPW
 #define MM3_TOPK_RPW 4
+#endif
+#ifndef MM3_TOPK_LANES
+#define MM3_TOPK_LANES 1
 #endif
 
 template <bool SPARSE, int RPW, bool ROWB>
@@ -268,13 +553,36 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((topk_kernel<0, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
 }
 
+// One lane per row: rows enough for 1024 waves (every SIMD of the chip),
+// topk within the kept list, rows that fit the registers, and score rows
+// that float4 loads can read.
+static bool lanes_fit(const TopkArgs& a, int64_t rows) {
+  return rows >= 65536 && a.topk <= kLaneTop && a.nb_max <= 128 && a.s_bytes > 0 &&
+         (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && a.s_row % 4 == 0 &&
+         (a.heads == 1 || a.s_head % 4 == 0);
+}
+
+template <bool ROWB>
+static void launch_topk_lanes(const TopkArgs& a, hipStream_t s) {
+  dim3 grid((a.rows.tokens + 255) / 256, a.heads), block(256);
+  if (a.nb_max <= 64)
+    hipLaunchKernelGGL((topk_lanes_kernel<4, ROWB>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB>), grid, block, 0, s, a);
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   // several rows per wave only when there are rows enough to keep every
   // wave slot of the chip busy that way (prefill-sized batches)
   const int64_t rows = (int64_t)a.rows.tokens * a.heads;
   const bool multi = MM3_TOPK_RPW > 1 && rows >= 65536 && a.nb_max <= 1024;
   const bool rowb = a.row_blocks != nullptr;
-  if (a.sparse)
+  if (!a.sparse && MM3_TOPK_LANES && lanes_fit(a, rows)) {
+    if (rowb)
+      launch_topk_lanes<true>(a, s);
+    else
+      launch_topk_lanes<false>(a, s);
+  } else if (a.sparse)
     launch_topk_t<true, 1, false>(a, s);
   else if (multi && rowb)
     launch_topk_t<false, MM3_TOPK_RPW, true>(a, s);

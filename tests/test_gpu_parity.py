@@ -730,3 +730,42 @@ def test_topk_blocks_many_rows():
     torch.cuda.synchronize()
     want = _oracle_by_blocks(s.cpu().numpy(), nv.cpu().numpy(), 16, 1, 2)
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("mode,nb,topk,I,L", [
+    ("positions", 64, 16, 1, 2), ("positions", 128, 5, 0, 0), ("positions", 100, 16, 8, 8),
+    ("blocks", 64, 3, 1, 1), ("blocks", 128, 16, 0, 2)])
+def test_lane_selector(mode, nb, topk, I, L):
+    """From 65536 (row, head) pairs, with topk <= 16 and at most 128 blocks,
+    each lane selects one row by itself (sorting networks instead of the
+    ballot search).  Coarse scores (many exact ties, -0.0 beside +0.0),
+    small topk, forced blocks filling every slot, and rows narrower than
+    the 16-block chunks the lanes read: ids equal the oracle's exactly."""
+    import oracle
+    H, R, Q = 2, 8, 5000
+    T = R * Q
+    assert H * T >= 65536
+    W = nb  # a multiple of 4: 16-byte aligned rows
+    g = torch.Generator(device=DEV).manual_seed(83 + nb + topk)
+    s = torch.randint(-6, 6, (H, T, W), generator=g, device=DEV).float() * 0.5
+    flip = torch.rand((H, T, W), generator=g, device=DEV) < 0.5
+    s = torch.where((s == 0) & flip, torch.full_like(s, -0.0), s)
+    if mode == "positions":
+        seq = torch.randint(Q, 128 * nb + 1, (R,), generator=g, device=DEV).to(torch.int32)
+        pos = (seq.long() - Q).repeat_interleave(Q) + torch.arange(Q, device=DEV).repeat(R)
+        nv = (pos // 128 + 1).to(torch.int32)
+    else:
+        nv = torch.randint(0, nb + 1, (T,), generator=g, device=DEV).to(torch.int32)
+    cols = torch.arange(W, device=DEV)
+    s = torch.where(cols[None, None, :] >= nv[None, :, None].long(), torch.full_like(s, float("nan")), s)
+    out = torch.full((H, T, topk), -7, dtype=torch.int32, device=DEV)
+    _say(f"lane selector: {mode} nb={nb} topk={topk} I={I} L={L}")
+    if mode == "positions":
+        mm3.mm3_index_topk(s, seq, Q, 128 * nb, topk, I, L, out=out)
+        torch.cuda.synchronize()
+        want = oracle.topk(s.cpu().numpy(), seq.cpu().numpy(), Q, topk, I, L)
+    else:
+        mm3.mm3_index_topk_blocks(s, nv, 128 * nb, topk, I, L, out=out)
+        torch.cuda.synchronize()
+        want = _oracle_by_blocks(s.cpu().numpy(), nv.cpu().numpy(), topk, I, L)
+    assert np.array_equal(out.cpu().numpy(), want)
