@@ -739,12 +739,13 @@ def test_lane_selector(mode, nb, topk, I, L):
     """From 65536 (row, head) pairs, with topk <= 16 and at most 128 blocks,
     each lane selects one row by itself (sorting networks instead of the
     ballot search).  Coarse scores (many exact ties, -0.0 beside +0.0),
-    small topk, forced blocks filling every slot, and rows narrower than
-    the 16-block chunks the lanes read: ids equal the oracle's exactly."""
+    small topk, forced blocks filling every slot, rows narrower than the
+    16-block chunks the lanes read, and a last wave with fewer than 64
+    rows: ids equal the oracle's exactly."""
     import oracle
-    H, R, Q = 2, 8, 5000
+    H, R, Q = 2, 8, 5003
     T = R * Q
-    assert H * T >= 65536
+    assert H * T >= 65536 and T % 64 != 0  # the last wave holds fewer rows
     W = nb  # a multiple of 4: 16-byte aligned rows
     g = torch.Generator(device=DEV).manual_seed(83 + nb + topk)
     s = torch.randint(-6, 6, (H, T, W), generator=g, device=DEV).float() * 0.5
