@@ -85,6 +85,17 @@ def recorded_traffic(workload: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def selector_kernel(w) -> str:
+    """The selector kernel the library launches for this batch: one lane per
+    row from 65536 (head, row) pairs with topk <= 16 and at most 128 blocks
+    per row (the score rows bench.py allocates are aligned), else one wave
+    per row."""
+    nb = -(-w.max_seq_len // 128)
+    if w.heads * w.rows >= 65536 and w.topk <= 16 and nb <= 128:
+        return "topk_lanes_kernel"
+    return "topk_kernel"
+
+
 def algorithmic(w, seq):
     """Algorithmic work of one pass.  Requests with heads * rows <= 16 go to
     the decode scorer, whose unit is bytes: every visible key once, the query
@@ -351,7 +362,7 @@ def main():
         },
         "rows_per_s": round(rows_per_s, 1),
         "roofline": roof,
-        "selector": dict(kernel="topk_kernel", ms=round(ms_topk, 4),
+        "selector": dict(kernel=selector_kernel(base), ms=round(ms_topk, 4),
                          achieved_gbs=round(sel_gbs, 1), bytes=alg["selector_bytes"]),
         "step_ms_graph": None if ms_graph is None else round(ms_graph, 5),
         "scorer_ms_p10_p50_p90": pct_score,

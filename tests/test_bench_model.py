@@ -73,3 +73,17 @@ def test_bench_refuses_several_gpus(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_selector_kernel_follows_the_launch_rule():
+    # the benchmark names the selector kernel the library launches: one lane
+    # per row from 65536 (head, row) pairs with topk <= 16 and <= 128 blocks
+    from types import SimpleNamespace as W
+    chunked_prefill = W(heads=4, rows=32768, topk=16, max_seq_len=16384)
+    decode_batch = W(heads=4, rows=256, topk=16, max_seq_len=32768)
+    mixed_serving = W(heads=4, rows=8352, topk=16, max_seq_len=32768)
+    wide = W(heads=4, rows=32768, topk=16, max_seq_len=16385)   # 129 blocks
+    big_k = W(heads=4, rows=32768, topk=17, max_seq_len=16384)
+    assert bench.selector_kernel(chunked_prefill) == "topk_lanes_kernel"
+    for w in (decode_batch, mixed_serving, wide, big_k):
+        assert bench.selector_kernel(w) == "topk_kernel"
