@@ -770,3 +770,22 @@ def test_lane_selector(mode, nb, topk, I, L):
         torch.cuda.synchronize()
         want = _oracle_by_blocks(s.cpu().numpy(), nv.cpu().numpy(), topk, I, L)
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_fused_prefill_shape_lane_selector():
+    """mm3_index_decode on a prefill-sized batch (65600 (row, head) pairs,
+    rows not a multiple of 64): the selector runs one lane per row on the
+    scores in the caller's buffer and on those in the workspace; both give
+    the same ids, equal to the oracle's selection on the same scores."""
+    import oracle
+    w = make(name="fused_prefill", R=2, lens=(16384, 16384), Q=8200, H=4, max_seq_len=16384,
+             topk=16, I=1, L=2, kfmt=KFMT_BF16, seed=85, device=DEV)
+    assert w.rows * w.heads >= 65536 and w.rows % 64 != 0
+    _say(f"fused prefill shape: R={w.num_reqs} rows={w.rows} H={w.heads}")
+    scores, out = run_fused(w, with_scores=True)
+    _, out_ws = run_fused(w, with_scores=False)
+    assert torch.equal(out, out_ws)
+    want = oracle.topk(scores.cpu().numpy(), w.seq_lens.cpu().numpy(), w.query_len, w.topk,
+                       w.init_blocks, w.local_blocks)
+    assert np.array_equal(out.cpu().numpy(), want)
+    invariants(w, out)
