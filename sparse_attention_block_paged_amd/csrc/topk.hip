@@ -362,17 +362,23 @@ __device__ __forceinline__ void lane_chunk_load(f32x4 (&g)[4], const __amdgpu_bu
     g[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, roff[q], 64 * c, 0));
 }
 
-// Rows of 16*NC blocks at most; the score rows are 16-byte aligned and the
-// tensor spans s_bytes < 2 GiB (checked by the launcher).
-template <int NC, bool ROWB>
+// Rows of 16*NC*SPLIT blocks at most; the score rows are 16-byte aligned and
+// the tensor spans s_bytes < 2 GiB (checked by the launcher).  SPLIT lanes
+// share a row: lanes l and l + 32 (SPLIT == 2) take its blocks [0, 128) and
+// [128, 256), merge their kept lists after the sorting pass, and write their
+// ids one after the other (ties go to the lower half first).
+template <int NC, bool ROWB, int SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void topk_lanes_kernel(TopkArgs a) {
+  constexpr int RW = 64 / SPLIT;  // rows per wave
   __shared__ __attribute__((aligned(16))) float tr[4][64 * kLaneRowFloats];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y;
-  const int t0 = (blockIdx.x * 4 + wave) * 64;  // the wave's first row
+  const int t0 = (blockIdx.x * 4 + wave) * RW;  // the wave's first row
   if (t0 >= a.rows.tokens) return;
   const int T = a.rows.tokens;
-  const int t = t0 + lane;
+  const int half = lane / RW;   // which part of the row this lane takes
+  const int b0 = 128 * half;    // its first block
+  const int t = t0 + lane % RW;
   const bool live = t < T;
   const int tc = live ? t : T - 1;
   // The loads nv depends on go out first.  Memory loads retire in issue
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   } else {
     // the wave's rows lie in requests [r_lo, r_hi]
     const int r_lo = row_request(m, t0);
-    const int r_hi = row_request(m, min(t0 + 63, T - 1));
+    const int r_hi = row_request(m, min(t0 + RW - 1, T - 1));
     const int r = lane_request(m, tc, r_lo, r_hi);
     c0 = m.cu[r];
     c1 = m.cu[r + 1];
@@ -407,11 +413,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   // values are not used.
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.scores, (short)0, a.s_bytes, 0x00020000);
+  // load q, lane l: LDS row p = 16q + l/4, i.e. the part p / RW of the
+  // wave's row p % RW -- the row and part that lane p works on
   int roff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int tq = min(t0 + 16 * q + lane / 4, T - 1);
-    roff[q] = (int)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) + 16 * (lane % 4);
+    const int p = 16 * q + lane / 4;
+    const int tq = min(t0 + p % RW, T - 1);
+    roff[q] = (int)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) + 512 * (p / RW) + 16 * (lane % 4);
   }
   constexpr int PD = NC < kLaneAhead ? NC : kLaneAhead;  // chunks in flight
   f32x4 g[PD][4];
@@ -445,10 +454,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     f32x4 rv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) rv[j] = *reinterpret_cast<const f32x4*>(trw + lane * kLaneRowFloats + 4 * j);
-    // this chunk's visible blocks [16c, nv) and forced ones [16c, I) and
-    // [nv - L, nv), as bits of the chunk
-    const uint32_t vism = low_bits16(nv - 16 * c);
-    const uint32_t fm = low_bits16(I - 16 * c) | (vism & ~low_bits16(nv - L - 16 * c));
+    // this chunk's blocks from cb = b0 + 16c: visible ones [cb, nv) and
+    // forced ones [cb, I) and [nv - L, nv), as bits of the chunk
+    const int cb = b0 + 16 * c;
+    const uint32_t vism = low_bits16(nv - cb);
+    const uint32_t fm = low_bits16(I - cb) | (vism & ~low_bits16(nv - L - cb));
     uint32_t x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -465,6 +475,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     // the next chunk's exchange stays after this chunk's sort, so the loads
     // in flight have the sort's time to arrive
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (SPLIT == 2) {
+    // The lane swap leaves this lane's list in one copy and its partner's
+    // (lane ^ 32) in the other, the same way round for every entry; the 16
+    // largest of both are the row's.
+    uint32_t other[kLaneTop];
+#pragma unroll
+    for (int i = 0; i < kLaneTop; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(top[i], top[i], false, false);
+      top[i] = r[0];
+      other[i] = r[1];
+    }
+    merge16_desc(top, other);
   }
   const int K = a.topk;
   uint32_t thr = top[0];
@@ -492,6 +515,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     eqm[b / 32] |= eqb << (b % 32);
   }
   int left = thr != 0u ? need : 0;
+  if constexpr (SPLIT == 2) {
+    // the lower half's ties come first
+    int n_eq = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n_eq += __popc(eqm[w]);
+    const int n_lo = __shfl_xor(n_eq, 32);
+    if (half == 1) left = max(0, left - n_lo);
+  }
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     uint32_t x = eqm[w], keep = 0u;
@@ -509,20 +540,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     }
     selm[w] |= keep;
   }
+  // the upper half's ids follow the lower half's
+  int slot0 = 0;
+  if constexpr (SPLIT == 2) {
+    int n_sel = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n_sel += __popc(selm[w]);
+    const int n_lo = __shfl_xor(n_sel, 32);
+    slot0 = half == 1 ? n_lo : 0;
+  }
   if (!live) return;
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)tc * a.o_row;
-  for (int j = 0; j < K; ++j) {
+  for (int j = 0; slot0 + j < K; ++j) {
     int id = -1;
     bool found = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       if (!found && selm[w] != 0u) {
-        id = 32 * w + __builtin_ctz(selm[w]);
+        id = b0 + 32 * w + __builtin_ctz(selm[w]);
         selm[w] &= selm[w] - 1u;
         found = true;
       }
     }
-    orow[j] = id;
+    // the lower half of a split row writes its ids only; the upper half
+    // (or an unsplit row) pads the rest with -1
+    if (SPLIT == 1 || half == 1 || found) orow[slot0 + j] = id;
   }
 }
 
@@ -553,22 +595,32 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((topk_kernel<0, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
 }
 
-// One lane per row: rows enough for 1024 waves (every SIMD of the chip),
-// topk within the kept list, rows that fit the registers, and score rows
-// that float4 loads can read.
-static bool lanes_fit(const TopkArgs& a, int64_t rows) {
-  return rows >= 65536 && a.topk <= kLaneTop && a.nb_max <= 128 && a.s_bytes > 0 &&
-         (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && a.s_row % 4 == 0 &&
-         (a.heads == 1 || a.s_head % 4 == 0);
+// Lanes per row for the lane selector, or 0 for the wave-per-row one: rows
+// enough for about 1024 waves (every SIMD of the chip), topk within the kept
+// list, rows that fit the registers (128 blocks per lane), and score rows that
+// the 16-byte loads can read.
+#ifndef MM3_LANE2_MIN_ROWS
+#define MM3_LANE2_MIN_ROWS 32768
+#endif
+static int lanes_split(const TopkArgs& a, int64_t rows) {
+  const bool ok = a.topk <= kLaneTop && a.s_bytes > 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
+                  a.s_row % 4 == 0 && (a.heads == 1 || a.s_head % 4 == 0);
+  if (!ok) return 0;
+  if (a.nb_max <= 128) return rows >= 65536 ? 1 : 0;
+  if (a.nb_max <= 256) return rows >= MM3_LANE2_MIN_ROWS ? 2 : 0;
+  return 0;
 }
 
 template <bool ROWB>
-static void launch_topk_lanes(const TopkArgs& a, hipStream_t s) {
-  dim3 grid((a.rows.tokens + 255) / 256, a.heads), block(256);
-  if (a.nb_max <= 64)
-    hipLaunchKernelGGL((topk_lanes_kernel<4, ROWB>), grid, block, 0, s, a);
+static void launch_topk_lanes(const TopkArgs& a, int split, hipStream_t s) {
+  const int rows_per_wg = 4 * 64 / split;
+  dim3 grid((a.rows.tokens + rows_per_wg - 1) / rows_per_wg, a.heads), block(256);
+  if (split == 2)
+    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 2>), grid, block, 0, s, a);
+  else if (a.nb_max <= 64)
+    hipLaunchKernelGGL((topk_lanes_kernel<4, ROWB, 1>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 1>), grid, block, 0, s, a);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -577,11 +629,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.rows.tokens * a.heads;
   const bool multi = MM3_TOPK_RPW > 1 && rows >= 65536 && a.nb_max <= 1024;
   const bool rowb = a.row_blocks != nullptr;
-  if (!a.sparse && MM3_TOPK_LANES && lanes_fit(a, rows)) {
+  const int split = (!a.sparse && MM3_TOPK_LANES) ? lanes_split(a, rows) : 0;
+  if (split) {
     if (rowb)
-      launch_topk_lanes<true>(a, s);
+      launch_topk_lanes<true>(a, split, s);
     else
-      launch_topk_lanes<false>(a, s);
+      launch_topk_lanes<false>(a, split, s);
   } else if (a.sparse)
     launch_topk_t<true, 1, false>(a, s);
   else if (multi && rowb)

@@ -734,19 +734,22 @@ def test_topk_blocks_many_rows():
 
 @pytest.mark.parametrize("mode,nb,topk,I,L", [
     ("positions", 64, 16, 1, 2), ("positions", 128, 5, 0, 0), ("positions", 100, 16, 8, 8),
-    ("blocks", 64, 3, 1, 1), ("blocks", 128, 16, 0, 2)])
+    ("blocks", 64, 3, 1, 1), ("blocks", 128, 16, 0, 2),
+    ("positions", 256, 16, 1, 2), ("positions", 200, 7, 3, 4), ("blocks", 256, 16, 1, 2),
+    ("blocks", 129, 16, 0, 0)])
 def test_lane_selector(mode, nb, topk, I, L):
-    """From 65536 (row, head) pairs, with topk <= 16 and at most 128 blocks,
-    each lane selects one row by itself (sorting networks instead of the
-    ballot search).  Coarse scores (many exact ties, -0.0 beside +0.0),
-    small topk, forced blocks filling every slot, rows narrower than the
-    16-block chunks the lanes read, and a last wave with fewer than 64
-    rows: ids equal the oracle's exactly."""
+    """From 65536 (row, head) pairs with at most 128 blocks, or 32768 with
+    at most 256, and topk <= 16, lanes select rows by themselves (sorting
+    networks instead of the ballot search; two lanes per row past 128
+    blocks).  Coarse scores (many exact ties, -0.0 beside +0.0), small
+    topk, forced blocks filling every slot, rows narrower than the 16-block
+    chunks the lanes read, rows just past one lane's 128 blocks, and a last
+    wave with fewer rows than the others: ids equal the oracle's exactly."""
     import oracle
     H, R, Q = 2, 8, 5003
     T = R * Q
     assert H * T >= 65536 and T % 64 != 0  # the last wave holds fewer rows
-    W = nb  # a multiple of 4: 16-byte aligned rows
+    W = -(-nb // 4) * 4  # a multiple of 4: 16-byte aligned rows
     g = torch.Generator(device=DEV).manual_seed(83 + nb + topk)
     s = torch.randint(-6, 6, (H, T, W), generator=g, device=DEV).float() * 0.5
     flip = torch.rand((H, T, W), generator=g, device=DEV) < 0.5
