@@ -86,12 +86,14 @@ def recorded_traffic(workload: str, kernel: str):
 
 
 def selector_kernel(w) -> str:
-    """The selector kernel the library launches for this batch: one lane per
-    row from 65536 (head, row) pairs with topk <= 16 and at most 128 blocks
-    per row (the score rows bench.py allocates are aligned), else one wave
-    per row."""
+    """The selector kernel the library launches for this batch: lanes that
+    select rows by themselves (topk <= 16; one lane per row from 65536
+    (head, row) pairs with at most 128 blocks per row, two from 32768 pairs
+    with at most 256; the score rows bench.py allocates are aligned), else
+    one wave per row."""
     nb = -(-w.max_seq_len // 128)
-    if w.heads * w.rows >= 65536 and w.topk <= 16 and nb <= 128:
+    pairs = w.heads * w.rows
+    if w.topk <= 16 and ((nb <= 128 and pairs >= 65536) or (128 < nb <= 256 and pairs >= 32768)):
         return "topk_lanes_kernel"
     return "topk_kernel"
 

@@ -76,14 +76,17 @@ def test_bench_refuses_several_gpus(monkeypatch, capsys):
 
 
 def test_selector_kernel_follows_the_launch_rule():
-    # the benchmark names the selector kernel the library launches: one lane
-    # per row from 65536 (head, row) pairs with topk <= 16 and <= 128 blocks
+    # the benchmark names the selector kernel the library launches: lanes
+    # selecting rows by themselves for topk <= 16, from 65536 (head, row)
+    # pairs with <= 128 blocks or 32768 pairs with <= 256 blocks
     from types import SimpleNamespace as W
     chunked_prefill = W(heads=4, rows=32768, topk=16, max_seq_len=16384)
+    mixed_serving = W(heads=4, rows=8352, topk=16, max_seq_len=32768)     # 256 blocks
     decode_batch = W(heads=4, rows=256, topk=16, max_seq_len=32768)
-    mixed_serving = W(heads=4, rows=8352, topk=16, max_seq_len=32768)
-    wide = W(heads=4, rows=32768, topk=16, max_seq_len=16385)   # 129 blocks
+    few_short = W(heads=4, rows=8352, topk=16, max_seq_len=16384)         # 128 blocks
+    too_wide = W(heads=4, rows=32768, topk=16, max_seq_len=32769)         # 257 blocks
     big_k = W(heads=4, rows=32768, topk=17, max_seq_len=16384)
-    assert bench.selector_kernel(chunked_prefill) == "topk_lanes_kernel"
-    for w in (decode_batch, mixed_serving, wide, big_k):
+    for w in (chunked_prefill, mixed_serving):
+        assert bench.selector_kernel(w) == "topk_lanes_kernel"
+    for w in (decode_batch, few_short, too_wide, big_k):
         assert bench.selector_kernel(w) == "topk_kernel"
