@@ -342,6 +342,19 @@ __device__ __forceinline__ void cmp_bits(uint32_t k, uint32_t thr, uint32_t& gt,
       : "vcc");
 }
 
+// Sum of v over the parts below `part` of the row whose part-0 lane is rl
+// (parts sit 64/SPLIT lanes apart).  The whole wave must be active.
+template <int SPLIT>
+__device__ __forceinline__ int parts_below_t(int v, int rl, int part) {
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < SPLIT - 1; ++k) {
+    const int x = __shfl(v, rl + k * (64 / SPLIT));
+    sum += k < part ? x : 0;
+  }
+  return sum;
+}
+
 // Per-wave LDS row of one chunk (16 scores), padded so that both the
 // chunk's writes (16 rows x 64 bytes per instruction) and the lanes' row
 // reads spread over the banks.
@@ -364,9 +377,10 @@ __device__ __forceinline__ void lane_chunk_load(f32x4 (&g)[4], const __amdgpu_bu
 
 // Rows of 16*NC*SPLIT blocks at most; the score rows are 16-byte aligned and
 // the tensor spans s_bytes < 2 GiB (checked by the launcher).  SPLIT lanes
-// share a row: lanes l and l + 32 (SPLIT == 2) take its blocks [0, 128) and
-// [128, 256), merge their kept lists after the sorting pass, and write their
-// ids one after the other (ties go to the lower half first).
+// share a row (1, 2 or 4; lanes l, l + 64/SPLIT, ...): part p takes its
+// blocks [128p, 128p + 128).  After the sorting pass the parts merge their
+// kept lists, ties go to the lower parts first, and each part writes its ids
+// after those of the parts below it.
 template <int NC, bool ROWB, int SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void topk_lanes_kernel(TopkArgs a) {
   constexpr int RW = 64 / SPLIT;  // rows per wave
@@ -378,6 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   const int T = a.rows.tokens;
   const int half = lane / RW;   // which part of the row this lane takes
   const int b0 = 128 * half;    // its first block
+  const int rl = lane % RW;     // the row's lane in part 0
   const int t = t0 + lane % RW;
   const bool live = t < T;
   const int tc = live ? t : T - 1;
@@ -476,10 +491,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     // in flight have the sort's time to arrive
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (SPLIT == 2) {
-    // The lane swap leaves this lane's list in one copy and its partner's
-    // (lane ^ 32) in the other, the same way round for every entry; the 16
-    // largest of both are the row's.
+  if constexpr (SPLIT >= 2) {
+    // A lane swap leaves this lane's list in one copy and its partner's in
+    // the other, the same way round for every entry, so merging the two
+    // gives the 16 largest of both: with lane ^ 32, then (4 parts) with
+    // lane ^ 16.
     uint32_t other[kLaneTop];
 #pragma unroll
     for (int i = 0; i < kLaneTop; ++i) {
@@ -488,6 +504,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
       other[i] = r[1];
     }
     merge16_desc(top, other);
+    if constexpr (SPLIT == 4) {
+#pragma unroll
+      for (int i = 0; i < kLaneTop; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(top[i], top[i], false, false);
+        top[i] = r[0];
+        other[i] = r[1];
+      }
+      merge16_desc(top, other);
+    }
   }
   const int K = a.topk;
   uint32_t thr = top[0];
@@ -515,13 +540,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     eqm[b / 32] |= eqb << (b % 32);
   }
   int left = thr != 0u ? need : 0;
-  if constexpr (SPLIT == 2) {
-    // the lower half's ties come first
+  if constexpr (SPLIT >= 2) {
+    // the lower parts' ties come first
     int n_eq = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) n_eq += __popc(eqm[w]);
-    const int n_lo = __shfl_xor(n_eq, 32);
-    if (half == 1) left = max(0, left - n_lo);
+    left = max(0, left - parts_below_t<SPLIT>(n_eq, rl, half));
   }
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -540,14 +564,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     }
     selm[w] |= keep;
   }
-  // the upper half's ids follow the lower half's
+  // each part's ids follow those of the parts below it
   int slot0 = 0;
-  if constexpr (SPLIT == 2) {
+  if constexpr (SPLIT >= 2) {
     int n_sel = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) n_sel += __popc(selm[w]);
-    const int n_lo = __shfl_xor(n_sel, 32);
-    slot0 = half == 1 ? n_lo : 0;
+    slot0 = parts_below_t<SPLIT>(n_sel, rl, half);
   }
   if (!live) return;
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)tc * a.o_row;
@@ -562,9 +585,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
         found = true;
       }
     }
-    // the lower half of a split row writes its ids only; the upper half
-    // (or an unsplit row) pads the rest with -1
-    if (SPLIT == 1 || half == 1 || found) orow[slot0 + j] = id;
+    // the top part of the row (the whole row if unsplit) also pads the
+    // rest with -1; the others write their ids only
+    if (half == SPLIT - 1 || found) orow[slot0 + j] = id;
   }
 }
 
@@ -597,10 +620,13 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
 
 // Lanes per row for the lane selector, or 0 for the wave-per-row one: rows
 // enough for about 1024 waves (every SIMD of the chip), topk within the kept
-// list, rows that fit the registers (128 blocks per lane), and score rows that
-// the 16-byte loads can read.
+// list, 128 blocks per lane (1, 2 or 4 lanes for rows of up to 128, 256 or
+// 512 blocks), and score rows that the 16-byte loads can read.
 #ifndef MM3_LANE2_MIN_ROWS
 #define MM3_LANE2_MIN_ROWS 32768
+#endif
+#ifndef MM3_LANE4_MIN_ROWS
+#define MM3_LANE4_MIN_ROWS 16384
 #endif
 static int lanes_split(const TopkArgs& a, int64_t rows) {
   const bool ok = a.topk <= kLaneTop && a.s_bytes > 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
@@ -608,6 +634,7 @@ static int lanes_split(const TopkArgs& a, int64_t rows) {
   if (!ok) return 0;
   if (a.nb_max <= 128) return rows >= 65536 ? 1 : 0;
   if (a.nb_max <= 256) return rows >= MM3_LANE2_MIN_ROWS ? 2 : 0;
+  if (a.nb_max <= 512) return rows >= MM3_LANE4_MIN_ROWS ? 4 : 0;
   return 0;
 }
 
@@ -615,7 +642,9 @@ template <bool ROWB>
 static void launch_topk_lanes(const TopkArgs& a, int split, hipStream_t s) {
   const int rows_per_wg = 4 * 64 / split;
   dim3 grid((a.rows.tokens + rows_per_wg - 1) / rows_per_wg, a.heads), block(256);
-  if (split == 2)
+  if (split == 4)
+    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 4>), grid, block, 0, s, a);
+  else if (split == 2)
     hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 2>), grid, block, 0, s, a);
   else if (a.nb_max <= 64)
     hipLaunchKernelGGL((topk_lanes_kernel<4, ROWB, 1>), grid, block, 0, s, a);

@@ -736,15 +736,17 @@ def test_topk_blocks_many_rows():
     ("positions", 64, 16, 1, 2), ("positions", 128, 5, 0, 0), ("positions", 100, 16, 8, 8),
     ("blocks", 64, 3, 1, 1), ("blocks", 128, 16, 0, 2),
     ("positions", 256, 16, 1, 2), ("positions", 200, 7, 3, 4), ("blocks", 256, 16, 1, 2),
-    ("blocks", 129, 16, 0, 0)])
+    ("blocks", 129, 16, 0, 0), ("positions", 512, 16, 1, 2), ("blocks", 384, 9, 2, 2),
+    ("blocks", 257, 16, 0, 0)])
 def test_lane_selector(mode, nb, topk, I, L):
-    """From 65536 (row, head) pairs with at most 128 blocks, or 32768 with
-    at most 256, and topk <= 16, lanes select rows by themselves (sorting
-    networks instead of the ballot search; two lanes per row past 128
-    blocks).  Coarse scores (many exact ties, -0.0 beside +0.0), small
+    """From 65536 (row, head) pairs with at most 128 blocks, 32768 with at
+    most 256 or 16384 with at most 512, and topk <= 16, lanes select rows by
+    themselves (sorting networks instead of the ballot search; two or four
+    lanes per row past 128 or 256 blocks).  Coarse scores (many exact ties, -0.0 beside +0.0), small
     topk, forced blocks filling every slot, rows narrower than the 16-block
-    chunks the lanes read, rows just past one lane's 128 blocks, and a last
-    wave with fewer rows than the others: ids equal the oracle's exactly."""
+    chunks the lanes read, rows just past one or two lanes' blocks, and a
+    last wave with fewer rows than the others: ids equal the oracle's
+    exactly."""
     import oracle
     H, R, Q = 2, 8, 5003
     T = R * Q
