@@ -78,15 +78,17 @@ def test_bench_refuses_several_gpus(monkeypatch, capsys):
 def test_selector_kernel_follows_the_launch_rule():
     # the benchmark names the selector kernel the library launches: lanes
     # selecting rows by themselves for topk <= 16, from 65536 (head, row)
-    # pairs with <= 128 blocks or 32768 pairs with <= 256 blocks
+    # pairs with <= 128 blocks, 32768 with <= 256 or 16384 with <= 512
     from types import SimpleNamespace as W
     chunked_prefill = W(heads=4, rows=32768, topk=16, max_seq_len=16384)
     mixed_serving = W(heads=4, rows=8352, topk=16, max_seq_len=32768)     # 256 blocks
     decode_batch = W(heads=4, rows=256, topk=16, max_seq_len=32768)
     few_short = W(heads=4, rows=8352, topk=16, max_seq_len=16384)         # 128 blocks
-    too_wide = W(heads=4, rows=32768, topk=16, max_seq_len=32769)         # 257 blocks
+    long_prefill = W(heads=4, rows=8192, topk=16, max_seq_len=65536)      # 512 blocks
+    nvfp4_decode = W(heads=1, rows=512, topk=16, max_seq_len=65536)
+    too_wide = W(heads=4, rows=32768, topk=16, max_seq_len=65537)         # 513 blocks
     big_k = W(heads=4, rows=32768, topk=17, max_seq_len=16384)
-    for w in (chunked_prefill, mixed_serving):
+    for w in (chunked_prefill, mixed_serving, long_prefill):
         assert bench.selector_kernel(w) == "topk_lanes_kernel"
-    for w in (decode_batch, few_short, too_wide, big_k):
+    for w in (decode_batch, few_short, nvfp4_decode, too_wide, big_k):
         assert bench.selector_kernel(w) == "topk_kernel"
