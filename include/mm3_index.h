@@ -73,6 +73,7 @@ extern "C" {
 #define MM3_HEAD_DIM 128  /* index head dimension */
 #define MM3_MAX_BLOCKS 65534 /* cdiv(max_seq_len, 128) must stay below 65535 */
 #define MM3_MAX_TOPK 1024
+#define MM3_MAX_ROWS 2147482624 /* total_q bound: 2^31 - 1024 (grids round rows up to whole workgroups) */
 
 /*
  * How rows map to requests and positions (see "Rows" above).
@@ -86,7 +87,8 @@ extern "C" {
  *   query_len    >= 1: rows per request; with cu_seqlens_q, a bound on every
  *                n_r (the pages' max_query_len), which sizes grids.
  *   total_q      rows in all (tokens); == num_reqs * query_len without
- *                cu_seqlens_q.  Below 2^31, as is heads * query_len.
+ *                cu_seqlens_q.  At most MM3_MAX_ROWS (2^31 - 1024);
+ *                heads * query_len below 2^31.
  *   max_seq_len  capture-stable bound on every seq_lens[r] (e.g. the model's
  *                maximum length, not the batch maximum); sizes the grids.
  * The arrays live on the device and their VALUES are preconditions, not

@@ -51,6 +51,8 @@ int check_rows(const mm3_rows* m, int32_t heads) {
   if (m->query_len < 1) return fail(MM3_EINVAL, "query_len must be >= 1, got %d", m->query_len);
   if (m->num_reqs < 0) return fail(MM3_EINVAL, "num_reqs must be >= 0, got %d", m->num_reqs);
   if (m->total_q < 0) return fail(MM3_EINVAL, "total_q must be >= 0, got %d", m->total_q);
+  if (m->total_q > MM3_MAX_ROWS)
+    return fail(MM3_EINVAL, "total_q must be at most 2^31 - 1024, got %d", m->total_q);
   if (m->max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
   if (!m->seq_lens) return fail(MM3_EINVAL, "seq_lens must be non-NULL");
   if (!aligned(m->seq_lens, 4) || !aligned(m->cu_seqlens_q, 4) || !aligned(m->prefix_lens, 4))
@@ -322,6 +324,7 @@ int mm3_index_topk_blocks(const float* scores, int64_t s_head_stride, int64_t s_
                           int64_t o_row_stride, void* stream) {
   if (heads < 1) return fail(MM3_EINVAL, "heads must be >= 1");
   if (total_q < 0) return fail(MM3_EINVAL, "total_q must be >= 0, got %d", total_q);
+  if (total_q > MM3_MAX_ROWS) return fail(MM3_EINVAL, "total_q must be at most 2^31 - 1024, got %d", total_q);
   if (max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0");
   const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
   if (nb > MM3_MAX_BLOCKS)

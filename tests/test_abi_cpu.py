@@ -117,6 +117,7 @@ BAD_PROBLEMS = [
     ("rows_overflow", dict(heads=1 << 16, query_len=1 << 16, q_head_stride=128), "2^31"),
     ("total_q_mismatch", dict(total_q=31), "total_q"),
     ("total_q_negative", dict(cu_seqlens_q=FAKE * 8, total_q=-1), "total_q"),
+    ("total_q_past_grid_bound", dict(cu_seqlens_q=FAKE * 8, total_q=(1 << 31) - 1023), "2^31 - 1024"),
     ("prefix_without_cu", dict(prefix_lens=FAKE * 9), "prefix_lens needs cu_seqlens_q"),
     ("ragged_rows_without_requests", dict(cu_seqlens_q=FAKE * 8, num_reqs=0, total_q=5), "without requests"),
     ("cu_misaligned", dict(cu_seqlens_q=FAKE * 8 + 2), "aligned"),
@@ -318,6 +319,7 @@ BAD_TOPK_BLOCKS = [
     ("null_blocks", dict(rb=None), "row_blocks"),
     ("blocks_misaligned", dict(rb=FAKE * 4 + 2), "aligned"),
     ("negative_rows", dict(T=-1), "total_q"),
+    ("rows_past_grid_bound", dict(T=(1 << 31) - 1023), "2^31 - 1024"),
     ("forced_exceed", dict(topk=4, I=3, L=2, orow=4, oh=128), "exceeds"),
     ("score_width", dict(sw=10, sr=10, sh=320), "width"),
     ("head_stride", dict(sh=31 * 64), "head stride"),
