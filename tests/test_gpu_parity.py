@@ -794,3 +794,40 @@ def test_fused_prefill_shape_lane_selector():
                        w.init_blocks, w.local_blocks)
     assert np.array_equal(out.cpu().numpy(), want)
     invariants(w, out)
+
+
+@pytest.mark.parametrize("nb", [128, 256, 512])
+def test_graph_capture_lane_selector(nb):
+    """The lane selector (one, two or four lanes per row) captured once in a
+    HIP graph: replays after new scores and new lengths are written in place
+    match eager calls, with eager work and synchronisation between them."""
+    H, R, Q = 2, 4, 8200 if nb == 128 else 4100
+    T = R * Q
+    W = nb
+    s = torch.empty((H, T, W), device=DEV)
+    seq = torch.empty((R,), dtype=torch.int32, device=DEV)
+    out = torch.full((H, T, 16), -7, dtype=torch.int32, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(86 + nb)
+
+    def fill():
+        s.copy_(torch.randint(-20, 20, (H, T, W), generator=gen, device=DEV).float() * 0.125)
+        seq.copy_(torch.randint(Q, 128 * nb + 1, (R,), generator=gen, device=DEV).to(torch.int32))
+
+    fill()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        mm3.mm3_index_topk(s, seq, Q, 128 * nb, 16, 1, 2, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        mm3.mm3_index_topk(s, seq, Q, 128 * nb, 16, 1, 2, out=out)
+    want = torch.empty_like(out)
+    for it in range(3):
+        fill()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        mm3.mm3_index_topk(s, seq, Q, 128 * nb, 16, 1, 2, out=want)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"nb={nb}: replay {it} differs from eager"
