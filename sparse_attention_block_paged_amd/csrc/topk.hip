@@ -342,17 +342,17 @@ __device__ __forceinline__ void cmp_bits(uint32_t k, uint32_t thr, uint32_t& gt,
       : "vcc");
 }
 
-// Sum of v over the parts below `part` of the row whose part-0 lane is rl
-// (parts sit 64/SPLIT lanes apart).  The whole wave must be active.
+// Sum of v over the parts below `part` of a row (parts sit 64/SPLIT lanes
+// apart): a log-step scan over the parts.  The whole wave must be active.
 template <int SPLIT>
-__device__ __forceinline__ int parts_below_t(int v, int rl, int part) {
-  int sum = 0;
+__device__ __forceinline__ int parts_below_t(int v, int part) {
+  int incl = v;
 #pragma unroll
-  for (int k = 0; k < SPLIT - 1; ++k) {
-    const int x = __shfl(v, rl + k * (64 / SPLIT));
-    sum += k < part ? x : 0;
+  for (int d = 1; d < SPLIT; d <<= 1) {
+    const int x = __shfl_up(incl, d * (64 / SPLIT));
+    incl += part >= d ? x : 0;
   }
-  return sum;
+  return incl - v;
 }
 
 // Per-wave LDS row of one chunk (16 scores), padded so that both the
@@ -377,10 +377,10 @@ __device__ __forceinline__ void lane_chunk_load(f32x4 (&g)[4], const __amdgpu_bu
 
 // Rows of 16*NC*SPLIT blocks at most; the score rows are 16-byte aligned and
 // the tensor spans s_bytes < 2 GiB (checked by the launcher).  SPLIT lanes
-// share a row (1, 2 or 4; lanes l, l + 64/SPLIT, ...): part p takes its
-// blocks [128p, 128p + 128).  After the sorting pass the parts merge their
-// kept lists, ties go to the lower parts first, and each part writes its ids
-// after those of the parts below it.
+// share a row (a power of two up to 8; lanes l, l + 64/SPLIT, ...): part p
+// takes its blocks [16*NC*p, 16*NC*(p + 1)).  After the sorting pass the
+// parts merge their kept lists, ties go to the lower parts first, and each
+// part writes its ids after those of the parts below it.
 template <int NC, bool ROWB, int SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void topk_lanes_kernel(TopkArgs a) {
   constexpr int RW = 64 / SPLIT;  // rows per wave
@@ -391,8 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   if (t0 >= a.rows.tokens) return;
   const int T = a.rows.tokens;
   const int half = lane / RW;   // which part of the row this lane takes
-  const int b0 = 128 * half;    // its first block
-  const int rl = lane % RW;     // the row's lane in part 0
+  const int b0 = 16 * NC * half;  // its first block
   const int t = t0 + lane % RW;
   const bool live = t < T;
   const int tc = live ? t : T - 1;
@@ -435,7 +434,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   for (int q = 0; q < 4; ++q) {
     const int p = 16 * q + lane / 4;
     const int tq = min(t0 + p % RW, T - 1);
-    roff[q] = (int)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) + 512 * (p / RW) + 16 * (lane % 4);
+    roff[q] = (int)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) + 64 * NC * (p / RW) + 16 * (lane % 4);
   }
   constexpr int PD = NC < kLaneAhead ? NC : kLaneAhead;  // chunks in flight
   f32x4 g[PD][4];
@@ -492,24 +491,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (SPLIT >= 2) {
-    // A lane swap leaves this lane's list in one copy and its partner's in
-    // the other, the same way round for every entry, so merging the two
-    // gives the 16 largest of both: with lane ^ 32, then (4 parts) with
-    // lane ^ 16.
+    // Merge with the parts at lane distance 32, 16, ..., RW in turn.  A lane
+    // swap (distances 32 and 16) leaves this lane's list in one copy and its
+    // partner's in the other, the same way round for every entry; below 16 a
+    // lane shuffle brings the partner's.  Merging the two gives the 16
+    // largest of both.
     uint32_t other[kLaneTop];
 #pragma unroll
-    for (int i = 0; i < kLaneTop; ++i) {
-      const auto r = __builtin_amdgcn_permlane32_swap(top[i], top[i], false, false);
-      top[i] = r[0];
-      other[i] = r[1];
-    }
-    merge16_desc(top, other);
-    if constexpr (SPLIT == 4) {
+    for (int d = 32; d >= RW; d >>= 1) {
 #pragma unroll
       for (int i = 0; i < kLaneTop; ++i) {
-        const auto r = __builtin_amdgcn_permlane16_swap(top[i], top[i], false, false);
-        top[i] = r[0];
-        other[i] = r[1];
+        if (d == 32) {
+          const auto r = __builtin_amdgcn_permlane32_swap(top[i], top[i], false, false);
+          top[i] = r[0];
+          other[i] = r[1];
+        } else if (d == 16) {
+          const auto r = __builtin_amdgcn_permlane16_swap(top[i], top[i], false, false);
+          top[i] = r[0];
+          other[i] = r[1];
+        } else {
+          other[i] = (uint32_t)__shfl_xor((int)top[i], d);
+        }
       }
       merge16_desc(top, other);
     }
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     int n_eq = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) n_eq += __popc(eqm[w]);
-    left = max(0, left - parts_below_t<SPLIT>(n_eq, rl, half));
+    left = max(0, left - parts_below_t<SPLIT>(n_eq, half));
   }
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     int n_sel = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) n_sel += __popc(selm[w]);
-    slot0 = parts_below_t<SPLIT>(n_sel, rl, half);
+    slot0 = parts_below_t<SPLIT>(n_sel, half);
   }
   if (!live) return;
   int32_t* orow = a.out + (int64_t)h * a.o_head + (int64_t)tc * a.o_row;
@@ -618,10 +620,16 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((topk_kernel<0, SPARSE, RPW, ROWB>), grid, block, 0, s, a);
 }
 
-// Lanes per row for the lane selector, or 0 for the wave-per-row one: rows
-// enough for about 1024 waves (every SIMD of the chip), topk within the kept
-// list, 128 blocks per lane (1, 2 or 4 lanes for rows of up to 128, 256 or
-// 512 blocks), and score rows that the 16-byte loads can read.
+// Which form of the lane selector takes a batch, or none (split == 0: one
+// wave per row).  It needs topk within the kept list, score rows that the
+// 16-byte loads can read, and (head, row) pairs enough to keep the chip's
+// SIMDs busy.  A lane takes 16*kLaneChunks blocks of a row (64: registers
+// for four waves per SIMD), and 1, 2, 4 or 8 lanes share a row of up to 64,
+// 128, 256 or 512 blocks.
+#ifndef MM3_LANE_CHUNKS
+#define MM3_LANE_CHUNKS 4
+#endif
+constexpr int kLaneChunks = MM3_LANE_CHUNKS;
 #ifndef MM3_LANE2_MIN_ROWS
 #define MM3_LANE2_MIN_ROWS 32768
 #endif
@@ -631,25 +639,29 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
 static int lanes_split(const TopkArgs& a, int64_t rows) {
   const bool ok = a.topk <= kLaneTop && a.s_bytes > 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                   a.s_row % 4 == 0 && (a.heads == 1 || a.s_head % 4 == 0);
-  if (!ok) return 0;
-  if (a.nb_max <= 128) return rows >= 65536 ? 1 : 0;
-  if (a.nb_max <= 256) return rows >= MM3_LANE2_MIN_ROWS ? 2 : 0;
-  if (a.nb_max <= 512) return rows >= MM3_LANE4_MIN_ROWS ? 4 : 0;
-  return 0;
+  const int nb = a.nb_max;
+  if (!ok || nb > 512) return 0;
+  const int64_t min_rows = nb <= 128 ? 65536 : nb <= 256 ? MM3_LANE2_MIN_ROWS : MM3_LANE4_MIN_ROWS;
+  if (rows < min_rows) return 0;
+  int split = 1;
+  while (16 * kLaneChunks * split < nb) split *= 2;
+  return split;
 }
 
 template <bool ROWB>
 static void launch_topk_lanes(const TopkArgs& a, int split, hipStream_t s) {
+  constexpr int NC = kLaneChunks;
   const int rows_per_wg = 4 * 64 / split;
   dim3 grid((a.rows.tokens + rows_per_wg - 1) / rows_per_wg, a.heads), block(256);
-  if (split == 4)
-    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 4>), grid, block, 0, s, a);
-  else if (split == 2)
-    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 2>), grid, block, 0, s, a);
-  else if (a.nb_max <= 64)
-    hipLaunchKernelGGL((topk_lanes_kernel<4, ROWB, 1>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((topk_lanes_kernel<8, ROWB, 1>), grid, block, 0, s, a);
+  switch (split) {
+    case 1: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 4>), grid, block, 0, s, a); break;
+    default:
+      if constexpr (16 * NC * 8 >= 512)
+        hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 8>), grid, block, 0, s, a);
+      break;
+  }
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
