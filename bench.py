@@ -87,14 +87,14 @@ def recorded_traffic(workload: str, kernel: str):
 
 def selector_kernel(w) -> str:
     """The selector kernel the library launches for this batch: lanes that
-    select rows by themselves (topk <= 16; one lane per row from 65536
-    (head, row) pairs with at most 128 blocks per row, two from 32768 pairs
-    with at most 256, four from 16384 with at most 512; the score rows
-    bench.py allocates are aligned), else one wave per row."""
+    select rows by themselves when topk <= 16 and there are (head, row) pairs
+    enough (65536, 24576, 16384 or 8192 for rows of up to 64, 128, 256 or
+    512 blocks; the score rows bench.py allocates are aligned), else one
+    wave per row."""
     nb = -(-w.max_seq_len // 128)
     pairs = w.heads * w.rows
-    if w.topk <= 16 and ((nb <= 128 and pairs >= 65536) or (128 < nb <= 256 and pairs >= 32768)
-                         or (256 < nb <= 512 and pairs >= 16384)):
+    need = 65536 if nb <= 64 else 24576 if nb <= 128 else 16384 if nb <= 256 else 8192
+    if w.topk <= 16 and nb <= 512 and pairs >= need:
         return "topk_lanes_kernel"
     return "topk_kernel"
 

@@ -622,26 +622,35 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
 
 // Which form of the lane selector takes a batch, or none (split == 0: one
 // wave per row).  It needs topk within the kept list, score rows that the
-// 16-byte loads can read, and (head, row) pairs enough to keep the chip's
-// SIMDs busy.  A lane takes 16*kLaneChunks blocks of a row (64: registers
-// for four waves per SIMD), and 1, 2, 4 or 8 lanes share a row of up to 64,
-// 128, 256 or 512 blocks.
+// 16-byte loads can read, and (head, row) pairs enough for about one wave per
+// SIMD (below that the ballot search measured faster).  A lane takes
+// 16*kLaneChunks blocks of a row (64: registers for four waves per SIMD), and
+// 1, 2, 4 or 8 lanes share a row of up to 64, 128, 256 or 512 blocks.
 #ifndef MM3_LANE_CHUNKS
 #define MM3_LANE_CHUNKS 4
 #endif
 constexpr int kLaneChunks = MM3_LANE_CHUNKS;
+#ifndef MM3_LANE1_MIN_ROWS
+#define MM3_LANE1_MIN_ROWS 65536  // rows of up to 64 blocks
+#endif
 #ifndef MM3_LANE2_MIN_ROWS
-#define MM3_LANE2_MIN_ROWS 32768
+#define MM3_LANE2_MIN_ROWS 24576  // up to 128
 #endif
 #ifndef MM3_LANE4_MIN_ROWS
-#define MM3_LANE4_MIN_ROWS 16384
+#define MM3_LANE4_MIN_ROWS 16384  // up to 256
+#endif
+#ifndef MM3_LANE8_MIN_ROWS
+#define MM3_LANE8_MIN_ROWS 8192   // up to 512
 #endif
 static int lanes_split(const TopkArgs& a, int64_t rows) {
   const bool ok = a.topk <= kLaneTop && a.s_bytes > 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                   a.s_row % 4 == 0 && (a.heads == 1 || a.s_head % 4 == 0);
   const int nb = a.nb_max;
   if (!ok || nb > 512) return 0;
-  const int64_t min_rows = nb <= 128 ? 65536 : nb <= 256 ? MM3_LANE2_MIN_ROWS : MM3_LANE4_MIN_ROWS;
+  const int64_t min_rows = nb <= 64    ? MM3_LANE1_MIN_ROWS
+                           : nb <= 128 ? MM3_LANE2_MIN_ROWS
+                           : nb <= 256 ? MM3_LANE4_MIN_ROWS
+                                       : MM3_LANE8_MIN_ROWS;
   if (rows < min_rows) return 0;
   int split = 1;
   while (16 * kLaneChunks * split < nb) split *= 2;

@@ -77,18 +77,21 @@ def test_bench_refuses_several_gpus(monkeypatch, capsys):
 
 def test_selector_kernel_follows_the_launch_rule():
     # the benchmark names the selector kernel the library launches: lanes
-    # selecting rows by themselves for topk <= 16, from 65536 (head, row)
-    # pairs with <= 128 blocks, 32768 with <= 256 or 16384 with <= 512
+    # selecting rows by themselves for topk <= 16, from 65536, 24576, 16384
+    # or 8192 (head, row) pairs for rows of up to 64, 128, 256 or 512 blocks
     from types import SimpleNamespace as W
-    chunked_prefill = W(heads=4, rows=32768, topk=16, max_seq_len=16384)
-    mixed_serving = W(heads=4, rows=8352, topk=16, max_seq_len=32768)     # 256 blocks
-    decode_batch = W(heads=4, rows=256, topk=16, max_seq_len=32768)
-    few_short = W(heads=4, rows=8352, topk=16, max_seq_len=16384)         # 128 blocks
-    long_prefill = W(heads=4, rows=8192, topk=16, max_seq_len=65536)      # 512 blocks
-    nvfp4_decode = W(heads=1, rows=512, topk=16, max_seq_len=65536)
-    too_wide = W(heads=4, rows=32768, topk=16, max_seq_len=65537)         # 513 blocks
-    big_k = W(heads=4, rows=32768, topk=17, max_seq_len=16384)
-    for w in (chunked_prefill, mixed_serving, long_prefill):
-        assert bench.selector_kernel(w) == "topk_lanes_kernel"
-    for w in (decode_batch, few_short, nvfp4_decode, too_wide, big_k):
-        assert bench.selector_kernel(w) == "topk_kernel"
+    lanes = [W(heads=4, rows=32768, topk=16, max_seq_len=16384),     # chunked prefill
+             W(heads=4, rows=8352, topk=16, max_seq_len=32768),      # mixed serving
+             W(heads=4, rows=8192, topk=16, max_seq_len=65536),      # 512 blocks
+             W(heads=4, rows=6144, topk=16, max_seq_len=16384),      # 24576 pairs, 128 blocks
+             W(heads=4, rows=16384, topk=16, max_seq_len=8192)]      # 65536 pairs, 64 blocks
+    ballot = [W(heads=4, rows=256, topk=16, max_seq_len=32768),      # decode batch
+              W(heads=1, rows=512, topk=16, max_seq_len=65536),      # NVFP4 decode
+              W(heads=4, rows=8192, topk=16, max_seq_len=8192),      # 32768 pairs, 64 blocks
+              W(heads=4, rows=4096, topk=16, max_seq_len=16384),     # 16384 pairs, 128 blocks
+              W(heads=4, rows=32768, topk=16, max_seq_len=65537),    # 513 blocks
+              W(heads=4, rows=32768, topk=17, max_seq_len=16384)]    # topk 17
+    for w in lanes:
+        assert bench.selector_kernel(w) == "topk_lanes_kernel", w
+    for w in ballot:
+        assert bench.selector_kernel(w) == "topk_kernel", w

@@ -831,3 +831,30 @@ def test_graph_capture_lane_selector(nb):
         mm3.mm3_index_topk(s, seq, Q, 128 * nb, 16, 1, 2, out=want)
         torch.cuda.synchronize()
         assert torch.equal(got, want), f"nb={nb}: replay {it} differs from eager"
+
+
+@pytest.mark.parametrize("nb,topk", [(128, 20), (600, 16)])
+def test_ballot_selector_many_rows(nb, topk):
+    """Batches the lane selector does not take (topk above 16, rows past 512
+    blocks) run the wave-per-row search, several rows per wave from 65536
+    (head, row) pairs: ties, -0.0, NaN past each row's visible blocks; ids
+    equal the oracle's exactly."""
+    import oracle
+    H, R, Q = 2, 8, 5003
+    T = R * Q
+    W = -(-nb // 16) * 16
+    g = torch.Generator(device=DEV).manual_seed(87 + nb)
+    s = torch.randint(-6, 6, (H, T, W), generator=g, device=DEV).float() * 0.5
+    flip = torch.rand((H, T, W), generator=g, device=DEV) < 0.5
+    s = torch.where((s == 0) & flip, torch.full_like(s, -0.0), s)
+    seq = torch.randint(Q, 128 * nb + 1, (R,), generator=g, device=DEV).to(torch.int32)
+    pos = (seq.long() - Q).repeat_interleave(Q) + torch.arange(Q, device=DEV).repeat(R)
+    nv = pos // 128 + 1
+    cols = torch.arange(W, device=DEV)
+    s = torch.where(cols[None, None, :] >= nv[None, :, None], torch.full_like(s, float("nan")), s)
+    out = torch.full((H, T, topk), -7, dtype=torch.int32, device=DEV)
+    _say(f"ballot selector: nb={nb} topk={topk}")
+    mm3.mm3_index_topk(s, seq, Q, 128 * nb, topk, 1, 2, out=out)
+    torch.cuda.synchronize()
+    want = oracle.topk(s.cpu().numpy(), seq.cpu().numpy(), Q, topk, 1, 2)
+    assert np.array_equal(out.cpu().numpy(), want)
