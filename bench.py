@@ -61,16 +61,24 @@ PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 1 << 30
 
 
+# The kernels whose HBM traffic profiles/traffic.json records are the two
+# scorers: their sources, the headers they include, and the build script
+# (its per-source flags change their code).
+SCORER_SOURCES = ("decode_score.hip", "prefill_score.hip", "mm3_device.h", "mm3_fp4.h",
+                  "mm3_launch.h", "mm3_rows.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: recorded HBM traffic is only reported while
-    the kernels are the ones the counters were taken on."""
-    import glob
+    """Hash of the scorer kernels' sources and build flags: recorded HBM
+    traffic is only reported while the scorers are the ones the counters were
+    taken on."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_attention_block_paged_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    pkg = os.path.join(ROOT, "sparse_attention_block_paged_amd")
+    for f in SCORER_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(pkg, "csrc", f), "rb").read())
+    h.update(open(os.path.join(pkg, "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -244,25 +244,26 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(TopkArgs a) {
   }
 }
 
-// ---- one lane per row
+// ---- lanes that select rows by themselves
 //
-// For batches with many short rows (prefill chunks), each lane selects one
-// (head, row) pair by itself.  The selection then runs on the vector units,
-// 64 rows per instruction, instead of as the per-row ballot search above,
-// whose scalar popcounts, compares and branches all queue on the CU's one
-// scalar unit (about 8 scalar instructions per search step, ~15 steps per
-// row).  The wave reads its 64 rows in chunks of 16 blocks with coalesced
-// loads (64 contiguous bytes per row and chunk) and hands each lane its
-// row's chunk through LDS.  A lane keeps its whole row's keys (at most
-// 16*NC blocks) in registers, and the 16 largest of them sorted:
+// For batches with many rows (prefill chunks), lanes select (head, row) pairs
+// by themselves.  The selection then runs on the vector units, a wave's rows
+// in each instruction, instead of as the per-row ballot search above, whose
+// scalar popcounts, compares and branches all queue on the CU's one scalar
+// unit (about 8 scalar instructions per search step, ~15 steps per row).
+// SPLIT lanes share a row, each taking 16*NC of its blocks.  The wave reads
+// its rows in chunks of 16 blocks with coalesced loads (64 contiguous bytes
+// per row part and chunk) and hands each lane its chunk through LDS.  A lane
+// keeps its part's keys in registers, and the 16 largest of them sorted:
 //   * each chunk of 16 keys is sorted by a bitonic network;
 //   * the elementwise max of the kept list (descending) and the reversed
 //     chunk holds the 16 largest of both, as a bitonic sequence;
 //   * a half-cleaner cascade sorts it again.
-// The topk-th kept key is the threshold T.  A second pass over the registers
-// takes the blocks above T, and those equal to T in ascending id order until
-// topk are chosen: the same set as the ballot search, written in the same
-// ascending order.
+// The lanes of a row then merge their kept lists the same way.  The topk-th
+// kept key is the threshold T.  A second pass over the registers takes the
+// blocks above T, and those equal to T in ascending id order until topk are
+// chosen: the same set as the ballot search, written in the same ascending
+// order.
 constexpr int kLaneTop = 16;  // kept keys per lane: topk <= 16
 
 __device__ __forceinline__ void cx_desc(uint32_t& hi, uint32_t& lo) {
