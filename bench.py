@@ -8,14 +8,20 @@ max) and the top-k selector, as one mm3_index_decode call (workloads 1, 2, 3,
 6; the ragged serving batch, workload 7, whose decode requests and prefill
 chunks share one call).
 
-Default workload: the 64-request decode batch (seq_len ~ U[4096, 32768],
-query_len 4, 4 index heads, topk 16, 1 init + 2 local blocks).
+Default workload (the JSON line's value): the high-batch long decode, the
+largest single-GPU workload -- 256 requests, seq_len ~ U[32768, 131072],
+query_len 4, 1 index head, topk 16, 1 init + 2 local blocks, through the
+fused mm3_index_decode call.  The same run times the other workloads
+(tiny decode latency, decode batch, chunked prefill, NVFP4 decode) under
+"extras", each with its own roofline fraction.
 
 Prints ONE JSON line.  Besides the contract fields it carries
   roofline      the dominant kernel (the scorer) against MI355X peak, from
                 HIP-event timing of that kernel alone inside this run;
-  cpu_baseline  the CPU oracle on this host, on a bounded sample;
-  selector      the top-k kernel's own timing.
+  cpu_baseline  the CPU oracle on this host, on a bounded sample, with its
+                scoring and selection timed separately;
+  selector      the top-k kernel's own timing;
+  extras        the other workloads, measured the same way.
 Inputs rotate between two copies of the page pool so that successive steps
 do not hit in the 256 MB Infinity Cache.
 """
@@ -33,6 +39,8 @@ sys.path.insert(0, ROOT)
 METRIC = "index-K tokens scored/s + top-k rows/s; % HBM peak (decode), % MFMA (prefill)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, datasheet
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, datasheet
+HEADLINE = 3                 # the largest workload that fits one GPU
+EXTRAS = (1, 2, 4, 5)
 
 
 def parse():
@@ -40,10 +48,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=HEADLINE, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--copies", type=int, default=2, help="page-pool copies rotated per step")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph (step_ms_graph)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only --config (no extra workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU work for the oracle baseline")
@@ -93,20 +103,6 @@ def recorded_traffic(workload: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def selector_kernel(w) -> str:
-    """The selector kernel the library launches for this batch: lanes that
-    select rows by themselves when topk <= 16 and there are (head, row) pairs
-    enough (65536, 24576, 16384 or 8192 for rows of up to 64, 128, 256 or
-    512 blocks; the score rows bench.py allocates are aligned), else one
-    wave per row."""
-    nb = -(-w.max_seq_len // 128)
-    pairs = w.heads * w.rows
-    need = 65536 if nb <= 64 else 24576 if nb <= 128 else 16384 if nb <= 256 else 8192
-    if w.topk <= 16 and nb <= 512 and pairs >= need:
-        return "topk_lanes_kernel"
-    return "topk_kernel"
-
-
 def algorithmic(w, seq):
     """Algorithmic work of one pass.  Requests with heads * rows <= 16 go to
     the decode scorer, whose unit is bytes: every visible key once, the query
@@ -144,40 +140,22 @@ def algorithmic(w, seq):
                 flops=flops, tokens=tokens, rows=H * T, pairs=pairs)
 
 
-def main():
-    args = parse()
-    if args.summarize_rocprof:
-        summarize_rocprof(args.summarize_rocprof, args.label, args.record_traffic)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: the indexer runs on one GPU; --gpus above 1 is not supported "
-              "(requests would shard across GPUs with no exchange between them)",
-              file=sys.stderr)
-        sys.exit(2)
-
-    # oracle worker processes for the all-cores CPU baseline, started before
-    # anything touches the GPU (they import only numpy and the oracle)
-    pool, cores = None, 0
-    if not args.no_cpu_baseline:
-        import multiprocessing as mp
-        cores = max(1, min(16, os.cpu_count() or 1))
-        pool = mp.get_context("spawn").Pool(cores, initializer=_oracle_init)
+def measure(cid, torch, dev, steps, warmup, ncopies, graph=False, detail=True, keep=False):
+    """Time workload cid on the GPU: the whole step, then the scorer and the
+    selector alone (HIP events on the stream the library launches on).
+    Returns (results, workload) -- the workload only with keep, else its
+    device memory is released before returning."""
+    import dataclasses
 
     import numpy as np
-    import torch
 
     import sparse_attention_block_paged_amd as mm3
-    from workloads import WORKLOADS, config, host_subset
+    from workloads import WORKLOADS, config
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cid = args.config
     base = config(cid, device=dev)
     seq = base.seq_lens.cpu().numpy()
     copies = [base]
-    for _ in range(1, max(1, args.copies)):
-        import dataclasses
+    for _ in range(1, max(1, ncopies)):
         copies.append(dataclasses.replace(
             base, kdata=base.kdata.clone(),
             kscales=None if base.kscales is None else base.kscales.clone(),
@@ -237,7 +215,6 @@ def main():
 
     def per_launch(fn, n, warm):
         """Each launch bracketed by its own events: (p10, p50, p90) in ms."""
-        import numpy as np
         for i in range(warm):
             fn(i)
         torch.cuda.synchronize()
@@ -251,33 +228,25 @@ def main():
         t = np.array([a.elapsed_time(b) for a, b in ev])
         return [round(float(x), 4) for x in np.percentile(t, [10, 50, 90])]
 
-    if args.calibrate:  # known-size copy: scale reference for FETCH_SIZE / WRITE_SIZE
-        src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     # whole step (the contract's timed region)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / steps
 
     # the same step captured once per pool copy and replayed: the library
     # enqueues fixed grids with no allocation, so a step captures whole
     ms_graph = None
-    if args.graph:
+    if graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         graphs = []
@@ -291,19 +260,18 @@ def main():
                     step(c)
                 graphs.append(g)
         torch.cuda.synchronize()
-        ms_graph = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps, args.warmup)
+        ms_graph = timed(lambda i: graphs[i % len(graphs)].replay(), steps, warmup)
 
     # kernels alone, on the same stream (HIP events), same inputs
-    ms_score = timed(score_only, max(args.steps, 20), 3)
-    ms_topk = timed(topk_only, max(args.steps, 20), 3)
-    pct_score = per_launch(score_only, max(args.steps, 20), 3)
+    n_k = max(steps, 20)
+    ms_score = timed(score_only, n_k, 3)
+    ms_topk = timed(topk_only, n_k, 3)
+    pct_step = per_launch(step, n_k, 3)
+    pct_score = per_launch(score_only, n_k, 3) if detail else None
     # warm: the same pool copy every launch (keys partly in the 256 MB MALL)
-    ms_score_warm = timed(lambda i: score_only(0), max(args.steps, 20), 3)
-    copy_gbs = measured_copy_gbs(torch, dev)
+    ms_score_warm = timed(lambda i: score_only(0), n_k, 3) if detail else None
 
     alg = algorithmic(base, seq)
-    tokens_per_s = alg["tokens"] / (ms * 1e-3)
-    rows_per_s = alg["rows"] / (ms * 1e-3)
     if prefill and alg["scorer_bytes"]:
         # decode requests and prefill chunks in one call: both scorers run.
         # The bound is the time the two would take at peak (bytes at HBM
@@ -318,6 +286,7 @@ def main():
                     ms=round(ms_score, 4), per_launch_flops=alg["flops"],
                     per_launch_bytes=alg["scorer_bytes"],
                     combined="(bytes/8 TB/s + flops/2.5 PFLOP/s) / measured time, over both scorers")
+        step_frac = None
     elif prefill:
         achieved = alg["flops"] / (ms_score * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
@@ -325,6 +294,7 @@ def main():
                     traffic=recorded_traffic(base.name, "prefill_score_kernel<%d, true>" % base.kfmt),
                     kernel="prefill_score_kernel<%d, true>" % base.kfmt, ms=round(ms_score, 4),
                     per_launch_flops=alg["flops"])
+        step_frac = None
     else:
         achieved = alg["scorer_bytes"] / (ms_score * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -332,29 +302,22 @@ def main():
                     traffic=recorded_traffic(base.name, "decode_score_cu<%d>" % base.kfmt),
                     kernel="decode_score_cu<%d>" % base.kfmt, ms=round(ms_score, 4),
                     per_launch_bytes=alg["scorer_bytes"])
+        # the whole step (scorer + selector) against the scorer's bytes
+        step_frac = round(alg["scorer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     sel_gbs = alg["selector_bytes"] / (ms_topk * 1e-3) / 1e9
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(base, seq, args.cpu_seconds, pool, cores)
-        pool.close()
-        pool.join()
-
     cfg = WORKLOADS[cid]
-    line = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if base.kfmt == 0 else "nvfp4-keys/bf16",
-        "data": "synthetic",
-        "config": {
+    res = dict(
+        workload=base.name, config_id=cid, ms_per_step=ms, wall_s_timed=wall, ms_graph=ms_graph,
+        tokens_per_s=alg["tokens"] / (ms * 1e-3), rows_per_s=alg["rows"] / (ms * 1e-3),
+        roofline=roof, step_frac=step_frac, step_ms_p10_p50_p90=pct_step,
+        selector=dict(kernel=mm3.mm3_index_topk_selector(scores[0], base.rows, base.max_seq_len,
+                                                          base.topk),
+                      ms=round(ms_topk, 4), achieved_gbs=round(sel_gbs, 1),
+                      bytes=alg["selector_bytes"]),
+        scorer_ms_p10_p50_p90=pct_score,
+        scorer_ms_warm=None if ms_score_warm is None else round(ms_score_warm, 4),
+        prefill=prefill, tokens=alg["tokens"], rows=alg["rows"],
+        config={
             "workload": base.name,
             "num_reqs": base.num_reqs,
             "seq_len_range": list(cfg["lens"]),
@@ -371,16 +334,113 @@ def main():
             "path": "score+topk" if prefill else "fused mm3_index_decode",
             "pool_copies_rotated": len(copies),
         },
-        "rows_per_s": round(rows_per_s, 1),
-        "roofline": roof,
-        "selector": dict(kernel=selector_kernel(base), ms=round(ms_topk, 4),
-                         achieved_gbs=round(sel_gbs, 1), bytes=alg["selector_bytes"]),
-        "step_ms_graph": None if ms_graph is None else round(ms_graph, 5),
-        "scorer_ms_p10_p50_p90": pct_score,
-        "scorer_ms_warm": round(ms_score_warm, 4),
+        dtype="bf16" if base.kfmt == 0 else "nvfp4-keys/bf16")
+    if keep:
+        return res, base
+    del copies, outs, scores, wss, base
+    torch.cuda.empty_cache()
+    return res, None
+
+
+def extra_line(res):
+    """The short record of a workload timed beside the headline."""
+    r = res["roofline"]
+    e = {"config": res["config_id"], "ms_per_step": round(res["ms_per_step"], 5),
+         "step_ms_p10_p50_p90": res["step_ms_p10_p50_p90"],
+         "tokens_per_s": round(res["tokens_per_s"], 1), "rows_per_s": round(res["rows_per_s"], 1),
+         "roofline": {k: r[k] for k in ("bound", "kernel", "ms", "achieved", "unit", "frac")},
+         "selector": {k: res["selector"][k] for k in ("kernel", "ms")}}
+    if res["step_frac"] is not None:
+        e["step_frac_hbm"] = res["step_frac"]
+    if res["config_id"] == 1:
+        e["us_per_step"] = round(res["ms_per_step"] * 1e3, 2)
+        e["note"] = "latency only: 8 blocks of keys, too small for a roofline figure"
+    return e
+
+
+def main():
+    args = parse()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.label, args.record_traffic)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: the indexer runs on one GPU; --gpus above 1 is not supported "
+              "(requests would shard across GPUs with no exchange between them)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    # oracle worker processes for the all-cores CPU baseline, started before
+    # anything touches the GPU (they import only numpy and the oracle)
+    pool, cores = None, 0
+    if not args.no_cpu_baseline:
+        import multiprocessing as mp
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except (AttributeError, OSError):
+            cores = os.cpu_count() or 1
+        cores = max(1, min(16, cores))
+        pool = mp.get_context("spawn").Pool(cores, initializer=_oracle_init)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate:  # known-size copy: scale reference for FETCH_SIZE / WRITE_SIZE
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    res, base = measure(args.config, torch, dev, args.steps, args.warmup, args.copies,
+                        graph=args.graph, detail=True, keep=not args.no_cpu_baseline)
+    cpu = None
+    if not args.no_cpu_baseline:
+        seq = base.seq_lens.cpu().numpy()
+        cpu = cpu_baseline(base, seq, args.cpu_seconds, pool, cores)
+        pool.close()
+        pool.join()
+        del base
+        torch.cuda.empty_cache()
+
+    extras = {}
+    if not args.no_extras:
+        for cid in EXTRAS:
+            if cid == args.config:
+                continue
+            r, _ = measure(cid, torch, dev, min(args.steps, 20), 3, 1 if cid == 1 else args.copies,
+                           detail=False)
+            extras[r["workload"]] = extra_line(r)
+    copy_gbs = measured_copy_gbs(torch, dev)
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": res["dtype"],
+        "data": "synthetic",
+        "config": res["config"],
+        "rows_per_s": round(res["rows_per_s"], 1),
+        "roofline": res["roofline"],
+        "step_frac_hbm": res["step_frac"],
+        "selector": res["selector"],
+        "step_ms_graph": None if res["ms_graph"] is None else round(res["ms_graph"], 5),
+        "step_ms_p10_p50_p90": res["step_ms_p10_p50_p90"],
+        "scorer_ms_p10_p50_p90": res["scorer_ms_p10_p50_p90"],
+        "scorer_ms_warm": res["scorer_ms_warm"],
         "hbm_copy_measured_gbs": copy_gbs,
         "cpu_baseline": cpu,
-        "wall_s_timed": round(wall, 3),
+        "extras": extras,
+        "wall_s_timed": round(res["wall_s_timed"], 3),
     }
     print(json.dumps(line), flush=True)
 
@@ -481,16 +541,24 @@ def measured_copy_gbs(torch, dev, nbytes=1 << 30, reps=5):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def _oracle_job(job):
-    """One request through the oracle in a worker process (no torch, no GPU);
-    returns (worker pid, seconds spent in the oracle)."""
+def _oracle_run(a, rows_loc, topk, I, L, width):
+    """The oracle's two stages on one task: (scoring seconds, selection
+    seconds)."""
     import oracle
-    a, rows_loc, topk, I, L, width = job
     t0 = time.perf_counter()
-    oracle.forward(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
-                   a["seq_lens"], a["query_len"], a["sm_scale"], topk, I, L, width, rows=rows_loc,
-                   cu_seqlens_q=a["cu_seqlens_q"], prefix_lens=a["prefix_lens"])
-    return os.getpid(), time.perf_counter() - t0
+    s = oracle.block_scores(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
+                            a["seq_lens"], a["query_len"], a["sm_scale"], width, rows=rows_loc,
+                            cu_seqlens_q=a["cu_seqlens_q"], prefix_lens=a["prefix_lens"])
+    t1 = time.perf_counter()
+    oracle.topk(s, a["seq_lens"], a["query_len"], topk, I, L, rows=rows_loc,
+                cu_seqlens_q=a["cu_seqlens_q"], prefix_lens=a["prefix_lens"])
+    return t1 - t0, time.perf_counter() - t1
+
+
+def _oracle_job(job):
+    """One task in a worker process (no torch, no GPU): (worker pid, scoring
+    seconds, selection seconds)."""
+    return (os.getpid(), *_oracle_run(*job))
 
 
 def _oracle_init():
@@ -498,38 +566,71 @@ def _oracle_init():
     oracle.build(force=False)
 
 
+def _rates(tok, rows, t_score, t_sel, cores, kind_sample):
+    return {"value": round(tok / (t_score + t_sel), 1), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "sample": kind_sample,
+            "scoring": {"value": round(tok / t_score, 1), "unit": "tokens/s",
+                        "seconds": round(t_score, 3)},
+            "selection": {"value": round(rows / t_sel, 1), "unit": "rows/s",
+                          "seconds": round(t_sel, 3)}}
+
+
 def cpu_baseline_all_cores(tasks, pool, cores):
     """The same oracle tasks on the host cores this process may use (16 at
     most), one task at a time per worker process; the workers never touch the
-    GPU.  The time is the busiest worker's time inside the oracle: shipping a
-    request's pages to a worker process is not the oracle's work (the
-    transfer-inclusive wall time is reported beside it)."""
+    GPU.  The whole-path time is the busiest worker's time inside the oracle:
+    shipping a request's pages to a worker process is not the oracle's work
+    (the transfer-inclusive wall time is reported beside it).  Each stage's
+    time is its seconds summed over the workers, divided by the workers
+    used."""
     tok = sum(t[1] for t in tasks)
+    rows = sum(t[2] for t in tasks)
     t0 = time.perf_counter()
     res = pool.map(_oracle_job, [t[0] for t in tasks], chunksize=1)
     wall = time.perf_counter() - t0
     busy = {}
-    for pid, sec in res:
-        busy[pid] = busy.get(pid, 0.0) + sec
-    el = max(busy.values())
-    return {"value": round(tok / el, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"the same {len(tasks)} tasks over {len(busy)} of {cores} processes; busiest "
-                       f"worker {el:.2f} s in the oracle, {wall:.2f} s wall with the transfers")}
+    for pid, ts, tl in res:
+        b = busy.setdefault(pid, [0.0, 0.0])
+        b[0] += ts
+        b[1] += tl
+    n = len(busy)
+    el = max(sum(v) for v in busy.values())
+    ts = sum(v[0] for v in busy.values()) / n
+    tl = sum(v[1] for v in busy.values()) / n
+    out = _rates(tok, rows, ts, tl, cores,
+                 f"the same {len(tasks)} tasks over {n} of {cores} processes; busiest worker "
+                 f"{el:.2f} s in the oracle, {wall:.2f} s wall with the transfers; stage times "
+                 f"averaged over the workers")
+    out["value"] = round(tok / el, 1)
+    return out
+
+
+def _hash_arrays(h, a):
+    for k in ("q_bits", "kdata", "kscales", "block_table", "seq_lens", "cu_seqlens_q",
+              "prefix_lens"):
+        v = a.get(k)
+        if v is not None:
+            h.update(k.encode())
+            h.update(memoryview(v).cast("B") if v.flags.c_contiguous else v.tobytes())
 
 
 def cpu_baseline(w, seq, seconds, pool=None, cores=0):
     """The oracle as it is (single-threaded C, fp64) on this host, on the same
-    workload, about `seconds` of work.  Requests of up to 64 rows are done
-    whole, in order; longer ones (prefill chunks) in passes of 16 rows spread
-    over the request, one pass over every request at a time, until the time
-    is used.  Work is counted in the metric's unit: a request's visible keys
-    times the fraction of its rows done."""
-    import oracle
+    workload, about `seconds` of work: block scores, then the selection, each
+    timed on its own.  Requests of up to 64 rows are done whole, in order;
+    longer ones (prefill chunks) in passes of 16 rows spread over the
+    request, one pass over every request at a time, until the time is used.
+    Work is counted in the metric's units: a request's visible keys times the
+    fraction of its rows done (scoring), and (head, row) pairs selected
+    (selection).  The sampled inputs are hashed (sha256)."""
+    import hashlib
+
     from workloads import host_subset
     ranges = w.row_ranges()
     arrays = {}
-    tasks, tok, el, passes = [], 0.0, 0.0, 0
-    while el < seconds:
+    h = hashlib.sha256()
+    tasks, tok, rows_sel, t_score, t_sel, passes = [], 0.0, 0, 0.0, 0.0, 0
+    while t_score + t_sel < seconds:
         progressed = False
         for r in range(w.num_reqs):
             n = ranges[r][1]
@@ -540,37 +641,34 @@ def cpu_baseline(w, seq, seconds, pool=None, cores=0):
                 continue  # every row of this request is done
             if r not in arrays:
                 arrays[r] = host_subset(w, [r])[0]
+                _hash_arrays(h, arrays[r])
             a = arrays[r]
             rows_loc = list(range(passes, n, stride)) if n > 64 else None
-            t0 = time.perf_counter()
-            oracle.forward(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
-                           a["seq_lens"], a["query_len"], a["sm_scale"], w.topk, w.init_blocks,
-                           w.local_blocks, w.score_width, rows=rows_loc,
-                           cu_seqlens_q=a["cu_seqlens_q"], prefix_lens=a["prefix_lens"])
-            el += time.perf_counter() - t0
+            ts, tl = _oracle_run(a, rows_loc, w.topk, w.init_blocks, w.local_blocks, w.score_width)
+            t_score += ts
+            t_sel += tl
             nrows = n if rows_loc is None else len(rows_loc)
             vis = (int(a["prefix_lens"][0]) + n) if a["prefix_lens"] is not None else int(seq[r])
             t_tok = vis * nrows / n
             tok += t_tok
-            tasks.append(((a, rows_loc, w.topk, w.init_blocks, w.local_blocks, w.score_width), t_tok))
+            rows_sel += nrows * w.heads
+            tasks.append(((a, rows_loc, w.topk, w.init_blocks, w.local_blocks, w.score_width),
+                          t_tok, nrows * w.heads))
             progressed = True
-            if el >= seconds:
+            if t_score + t_sel >= seconds:
                 break
         passes += 1
         if not progressed:
             break
     reqs = len({id(t[0][0]) for t in tasks})
-    res = {
-        "value": round(tok / el, 1),
-        "unit": "tokens/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{len(tasks)} tasks over {reqs} of {w.num_reqs} requests (whole requests up to "
-                   f"64 rows; longer ones in passes of 16 rows), {int(tok)} tokens-equivalent, "
-                   f"{el:.1f} s, single-threaded fp64 C oracle"),
-        "host_cpus": os.cpu_count(),
-        "host_cpu_model": host_cpu_model(),
-    }
+    res = _rates(tok, rows_sel, t_score, t_sel, 1,
+                 f"{len(tasks)} tasks over {reqs} of {w.num_reqs} requests (whole requests up to "
+                 f"64 rows; longer ones in passes of 16 rows), {int(tok)} tokens-equivalent, "
+                 f"{rows_sel} (head, row) pairs, {t_score + t_sel:.1f} s, single-threaded fp64 C "
+                 f"oracle")
+    res["inputs_sha256"] = h.hexdigest()
+    res["host_cpus"] = os.cpu_count()
+    res["host_cpu_model"] = host_cpu_model()
     if pool is not None:
         try:
             res["all_cores"] = cpu_baseline_all_cores(tasks, pool, cores)

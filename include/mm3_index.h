@@ -269,6 +269,26 @@ int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride,
                                  int32_t topk, const mm3_rows* rows,
                                  const mm3_sparse_out* sparse, void* stream);
 
+/*
+ * mm3_index_topk_selector -- which selector kernel a selection call launches
+ * for a score tensor of this layout and these sizes: mm3_index_topk
+ * (by_row_blocks = 0, sparse = 0), mm3_index_topk_blocks (by_row_blocks = 1),
+ * or the selection inside mm3_index_decode (sparse = 1 when it builds the
+ * sparse block table; scores = the scores_out or workspace pointer it is
+ * given).  The kernels (one wave per row with a ballot search, or lanes that
+ * select rows by themselves) give identical ids; this names the one that
+ * runs, for tests and benchmarks.  Arguments as in those calls (scores is
+ * only inspected for its alignment).  Host only, no HIP call.
+ * Returns the kernel's name with its template arguments (host string, valid
+ * until the next call on this thread), or NULL with mm3_last_error() set for
+ * arguments those calls reject.
+ */
+const char* mm3_index_topk_selector(const float* scores, int64_t s_head_stride,
+                                    int64_t s_row_stride, int32_t s_width,
+                                    int32_t heads, int32_t total_q,
+                                    int32_t max_seq_len, int32_t topk,
+                                    int32_t by_row_blocks, int32_t sparse);
+
 /* Message for the last non-OK return on this thread ("" if none).  Host
  * pointer, valid until the next call on this thread. */
 const char* mm3_last_error(void);

@@ -56,7 +56,7 @@ def _load():
         lib.oracle_nvfp4_element.restype = ctypes.c_double
         lib.oracle_block_scores.argtypes = [
             P, I64, I64, I32, I32, P, P, I64, P, I64, P, I32, I32, P, P, F32,
-            P, I64, I64, P, I64]
+            P, P, I64, I64, P, I64]
         lib.oracle_block_scores.restype = I32
         lib.oracle_topk.argtypes = [
             P, I64, I64, I32, P, I32, I32, P, P, I32, I32, I32, P, I64, I64, P, I64]
@@ -116,8 +116,10 @@ def total_rows(seq_lens, query_len, cu_seqlens_q=None):
 
 def block_scores(q_bits, kfmt, kdata, kscales, block_table, seq_lens,
                  query_len, sm_scale, width, rows=None, out=None,
-                 cu_seqlens_q=None, prefix_lens=None):
+                 cu_seqlens_q=None, prefix_lens=None, out64=None):
     """Scores [H, T, width] fp32 (unwritten entries stay NaN).
+    out64: optional float64 array of the same shape that receives each score
+    before its rounding to fp32 (sm_scale * the fp64 block maximum).
 
     q_bits: uint16 [T, H, 128] (bf16 bit patterns); kfmt 0: kdata uint16
     [pages,128,128]; kfmt 1: kdata uint8 [pages,128,64] nibbles and kscales
@@ -144,12 +146,14 @@ def block_scores(q_bits, kfmt, kdata, kscales, block_table, seq_lens,
     if out is None:
         out = np.full((H, T, width), np.nan, dtype=np.float32)
     assert out.dtype == np.float32 and out.flags.c_contiguous
+    if out64 is not None:
+        assert out64.dtype == np.float64 and out64.flags.c_contiguous and out64.shape == out.shape
     rr, nr = _rows_arg(rows)
     rc = _load().oracle_block_scores(
         _ptr(q_bits), H * D, D, H, kfmt, _ptr(kdata),
         _ptr(kscales) if kfmt == 1 else None, kdata.shape[0], _ptr(bt),
         bt.shape[1], _ptr(sl), R, query_len, _ptr(cu), _ptr(pre),
-        float(sm_scale), _ptr(out), out.shape[1] * out.shape[2], out.shape[2],
+        float(sm_scale), _ptr(out), _ptr(out64), out.shape[1] * out.shape[2], out.shape[2],
         _ptr(rr), nr)
     if rc != 0:
         raise ValueError("oracle_block_scores rejected its arguments")
@@ -198,12 +202,17 @@ def sparse_block_table(topk_idx, seq_lens, query_len, abt, pages_per_block,
 
 def forward(q_bits, kfmt, kdata, kscales, block_table, seq_lens, query_len,
             sm_scale, topk_, init_blocks, local_blocks, width, rows=None,
-            cu_seqlens_q=None, prefix_lens=None):
-    """Scores then ids, the whole path on the CPU (rows: optional subset)."""
+            cu_seqlens_q=None, prefix_lens=None, with64=False):
+    """Scores then ids, the whole path on the CPU (rows: optional subset).
+    Returns (scores, ids), or (scores, scores64, ids) with with64."""
+    s64 = None
+    if with64:
+        T, H = np.asarray(q_bits).shape[:2]
+        s64 = np.full((H, T, width), np.nan, dtype=np.float64)
     s = block_scores(q_bits, kfmt, kdata, kscales, block_table, seq_lens,
                      query_len, sm_scale, width, rows=rows,
-                     cu_seqlens_q=cu_seqlens_q, prefix_lens=prefix_lens)
+                     cu_seqlens_q=cu_seqlens_q, prefix_lens=prefix_lens, out64=s64)
     # unwritten (invisible) entries are never read by the selection
     ids = topk(s, seq_lens, query_len, topk_, init_blocks, local_blocks, rows=rows,
                cu_seqlens_q=cu_seqlens_q, prefix_lens=prefix_lens)
-    return s, ids
+    return (s, s64, ids) if with64 else (s, ids)

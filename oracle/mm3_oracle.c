@@ -192,7 +192,11 @@ static double orc_key(int kfmt, const void* kdata, const uint8_t* kscales,
  *   nothing and are skipped.  For head h and visible block b <= pos/128:
  *     page = block_table[r][b], n = min(128, pos - 128 b + 1),
  *     score[h][t][b] = fl32( sm_scale * max_{s<n} sum_d q[t][h][d] k[page][s][d] ).
- * Blocks past pos/128 are not written.
+ * Blocks past pos/128 are not written.  scores64 (NULL allowed, same strides)
+ * receives the same value before its one rounding to fp32: two blocks whose
+ * scores64 are equal hold keys with the same largest dot product, a true
+ * tie, while equal fp32 scores may also come from distinct values that round
+ * alike.
  * Returns 0, or -1 on a bad argument (page id out of range, ...).
  */
 int oracle_block_scores(const uint16_t* q, int64_t q_tok_stride,
@@ -202,9 +206,9 @@ int oracle_block_scores(const uint16_t* q, int64_t q_tok_stride,
                         int64_t bt_row_stride, const int32_t* seq_lens,
                         int num_reqs, int query_len,
                         const int32_t* cu_seqlens_q, const int32_t* prefix_lens,
-                        float sm_scale, float* scores, int64_t s_head_stride,
-                        int64_t s_row_stride, const int64_t* rows,
-                        int64_t num_rows)
+                        float sm_scale, float* scores, double* scores64,
+                        int64_t s_head_stride, int64_t s_row_stride,
+                        const int64_t* rows, int64_t num_rows)
 {
     static orc_fp4_table table;
     if (kfmt == 1 && !table.ready)
@@ -241,8 +245,10 @@ int oracle_block_scores(const uint16_t* q, int64_t q_tok_stride,
                     if (dot > best)
                         best = dot;
                 }
-                scores[h * s_head_stride + t * s_row_stride + b] =
-                    (float)((double)sm_scale * best);
+                double v = (double)sm_scale * best;
+                scores[h * s_head_stride + t * s_row_stride + b] = (float)v;
+                if (scores64)
+                    scores64[h * s_head_stride + t * s_row_stride + b] = v;
             }
         }
     }

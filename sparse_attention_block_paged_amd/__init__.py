@@ -5,4 +5,5 @@ from ._binding import (BLOCK, HEAD_DIM, KFMT_BF16, KFMT_NVFP4, LIB_PATH, Mm3Erro
                        Problem, Rows, SparseOut, decode_workspace_bytes, lib, make_problem,
                        make_rows, make_sparse_out,
                        mm3_build_sparse_block_table, mm3_index_decode, mm3_index_score,
-                       mm3_index_topk, mm3_index_topk_blocks, score_width, version)
+                       mm3_index_topk, mm3_index_topk_blocks, mm3_index_topk_selector,
+                       score_width, version)

@@ -28,8 +28,8 @@ HEAD_DIM = 128
 
 EXPORTED = (
     "mm3_index_score", "mm3_index_topk", "mm3_index_topk_blocks", "mm3_index_decode_workspace_bytes",
-    "mm3_index_decode", "mm3_build_sparse_block_table", "mm3_last_error",
-    "mm3_version",
+    "mm3_index_decode", "mm3_build_sparse_block_table", "mm3_index_topk_selector",
+    "mm3_last_error", "mm3_version",
 )
 
 
@@ -111,6 +111,8 @@ def lib():
         L.mm3_index_decode.restype = ctypes.c_int
         L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, PR, PS, P]
         L.mm3_build_sparse_block_table.restype = ctypes.c_int
+        L.mm3_index_topk_selector.argtypes = [P, I64, I64, I32, I32, I32, I32, I32, I32, I32]
+        L.mm3_index_topk_selector.restype = ctypes.c_char_p
         L.mm3_last_error.argtypes = []
         L.mm3_last_error.restype = ctypes.c_char_p
         L.mm3_version.argtypes = []
@@ -376,6 +378,24 @@ def mm3_build_sparse_block_table(topk_idx, seq_lens, query_len, max_seq_len,
         topk_idx.data_ptr(), topk_idx.stride(0), K, ctypes.byref(rows), ctypes.byref(sp),
         _stream(topk_idx, stream)))
     return sparse_table, sparse_ctx_lens
+
+
+def mm3_index_topk_selector(scores, total_q, max_seq_len, topk, by_row_blocks=False,
+                            sparse=False) -> str:
+    """Name of the selector kernel a selection over this score tensor launches
+    (mm3_index_topk, mm3_index_topk_blocks with by_row_blocks, or the fused
+    decode's selection with its sparse table).  scores may be any tensor with
+    the layout (fp32 [heads, >=total_q, width], unit column stride); it is
+    not read."""
+    if scores.stride(-1) != 1 or scores.dim() != 3:
+        raise ValueError("scores must be [heads, tokens, width] with unit column stride")
+    name = lib().mm3_index_topk_selector(scores.data_ptr(), scores.stride(0), scores.stride(1),
+                                         scores.shape[2], scores.shape[0], int(total_q),
+                                         int(max_seq_len), int(topk), int(bool(by_row_blocks)),
+                                         int(bool(sparse)))
+    if name is None:
+        raise Mm3Error(MM3_EINVAL, lib().mm3_last_error().decode())
+    return name.decode()
 
 
 def version() -> str:

@@ -414,6 +414,37 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   return ok();
 }
 
+const char* mm3_index_topk_selector(const float* scores, int64_t s_head_stride, int64_t s_row_stride,
+                                    int32_t s_width, int32_t heads, int32_t total_q, int32_t max_seq_len,
+                                    int32_t topk, int32_t by_row_blocks, int32_t sparse) {
+  if (heads < 1) return fail(MM3_EINVAL, "heads must be >= 1"), nullptr;
+  if (total_q < 0 || total_q > MM3_MAX_ROWS)
+    return fail(MM3_EINVAL, "total_q must be in [0, 2^31 - 1024], got %d", total_q), nullptr;
+  if (max_seq_len < 0) return fail(MM3_EINVAL, "max_seq_len must be >= 0"), nullptr;
+  const int64_t nb = cdiv64(max_seq_len, MM3_BLOCK);
+  if (nb > MM3_MAX_BLOCKS)
+    return fail(MM3_EINVAL, "cdiv(max_seq_len,128) = %lld must be below 65535", (long long)nb), nullptr;
+  if (topk < 1 || topk > MM3_MAX_TOPK) return fail(MM3_EINVAL, "topk must be in [1, 1024], got %d", topk), nullptr;
+  if (s_width < nb) return fail(MM3_EINVAL, "score width < cdiv(max_seq_len,128)"), nullptr;
+  if (s_head_stride < 0 || s_row_stride < 0) return fail(MM3_EINVAL, "score strides must be non-negative"), nullptr;
+  if (sparse && (heads != 1 || by_row_blocks))
+    return fail(MM3_EINVAL, "the sparse block table is built for one index head, from positions"), nullptr;
+  TopkArgs a{};
+  a.scores = scores;
+  a.s_head = s_head_stride;
+  a.s_row = s_row_stride;
+  a.s_width = s_width;
+  a.rows.tokens = total_q;
+  a.heads = heads;
+  a.topk = topk;
+  a.nb_max = (int32_t)nb;
+  a.sparse = sparse ? 1 : 0;
+  a.row_blocks = by_row_blocks ? reinterpret_cast<const int32_t*>(16) : nullptr;  // only tested for NULL
+  a.s_bytes = score_bytes(s_head_stride, s_row_stride, s_width, heads, total_q);
+  g_err.clear();
+  return topk_kernel_name(a);
+}
+
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, int32_t topk,
                                  const mm3_rows* rows, const mm3_sparse_out* sparse, void* stream) {
   if (!topk_idx || !sparse)

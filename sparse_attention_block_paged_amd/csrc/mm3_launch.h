@@ -95,6 +95,9 @@ hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_prefill_score_nvfp4(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// The selector kernel launch_topk runs for these arguments, as its name and
+// template arguments (host only; the string lives until the thread's next call).
+const char* topk_kernel_name(const TopkArgs& a);
 hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s);
 
 // Rows one decode-scorer MFMA tile holds (heads * query_len must fit).

@@ -19,6 +19,8 @@
 // its output slot, so the row is written already sorted.  This replaces the
 // pages' packed 64-bit (score, id) keys and partial-top-k merges with a
 // single-pass threshold select that needs no workspace.
+#include <stdio.h>
+
 #include "mm3_device.h"
 #include "mm3_launch.h"
 #include "mm3_rows.h"
@@ -370,10 +372,10 @@ constexpr int kLaneAhead = MM3_LANE_AHEAD;
 // takes rows 16q + l/4 (l = lane), 16 bytes each at column 4*(l%4) of the
 // chunk, so each instruction reads 16 runs of 64 contiguous bytes.
 __device__ __forceinline__ void lane_chunk_load(f32x4 (&g)[4], const __amdgpu_buffer_rsrc_t& rs,
-                                                const int (&roff)[4], int c) {
+                                                const uint32_t (&roff)[4], int c) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    g[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, roff[q], 64 * c, 0));
+    g[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)roff[q], 64 * c, 0));
 }
 
 // Rows of 16*NC*SPLIT blocks at most; the score rows are 16-byte aligned and
@@ -430,12 +432,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
       __builtin_amdgcn_make_buffer_rsrc((void*)a.scores, (short)0, a.s_bytes, 0x00020000);
   // load q, lane l: LDS row p = 16q + l/4, i.e. the part p / RW of the
   // wave's row p % RW -- the row and part that lane p works on
-  int roff[4];
+  // Offsets are unsigned: a row near the end of a tensor of almost 2 GiB can
+  // reach past 2^31 here; such bytes lie past the descriptor's range, read as
+  // zeros, and belong to blocks past nv.
+  uint32_t roff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int p = 16 * q + lane / 4;
     const int tq = min(t0 + p % RW, T - 1);
-    roff[q] = (int)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) + 64 * NC * (p / RW) + 16 * (lane % 4);
+    roff[q] = (uint32_t)(((int64_t)h * a.s_head + (int64_t)tq * a.s_row) * 4) +
+              (uint32_t)(64 * NC * (p / RW) + 16 * (lane % 4));
   }
   constexpr int PD = NC < kLaneAhead ? NC : kLaneAhead;  // chunks in flight
   f32x4 g[PD][4];
@@ -631,6 +637,9 @@ static void launch_topk_t(const TopkArgs& a, hipStream_t s) {
 #define MM3_LANE_CHUNKS 4
 #endif
 constexpr int kLaneChunks = MM3_LANE_CHUNKS;
+// 16*kLaneChunks blocks per lane and at most 8 lanes per row must cover the
+// 512-block rows the lane path accepts.
+static_assert(kLaneChunks >= 4 && kLaneChunks % 2 == 0, "lane selector chunks");
 #ifndef MM3_LANE1_MIN_ROWS
 #define MM3_LANE1_MIN_ROWS 65536  // rows of up to 64 blocks
 #endif
@@ -655,7 +664,7 @@ static int lanes_split(const TopkArgs& a, int64_t rows) {
   if (rows < min_rows) return 0;
   int split = 1;
   while (16 * kLaneChunks * split < nb) split *= 2;
-  return split;
+  return split <= 8 ? split : 0;
 }
 
 template <bool ROWB>
@@ -667,34 +676,65 @@ static void launch_topk_lanes(const TopkArgs& a, int split, hipStream_t s) {
     case 1: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 2>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 4>), grid, block, 0, s, a); break;
-    default:
-      if constexpr (16 * NC * 8 >= 512)
-        hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 8>), grid, block, 0, s, a);
-      break;
+    case 8: hipLaunchKernelGGL((topk_lanes_kernel<NC, ROWB, 8>), grid, block, 0, s, a); break;
+    default: break;  // lanes_split returns 1, 2, 4 or 8 only
   }
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+// Which selector kernel takes a batch: the lane selector (split lanes per
+// row), or one wave per row (rpw rows per wave, E keys per lane, 0 for the
+// form that re-reads long rows).
+struct TopkPlan {
+  int split;
+  int rpw;
+  int E;
+  bool sparse;
+  bool rowb;
+};
+
+static TopkPlan plan_topk(const TopkArgs& a) {
+  TopkPlan p{};
   // several rows per wave only when there are rows enough to keep every
   // wave slot of the chip busy that way (prefill-sized batches)
   const int64_t rows = (int64_t)a.rows.tokens * a.heads;
   const bool multi = MM3_TOPK_RPW > 1 && rows >= 65536 && a.nb_max <= 1024;
-  const bool rowb = a.row_blocks != nullptr;
-  const int split = (!a.sparse && MM3_TOPK_LANES) ? lanes_split(a, rows) : 0;
-  if (split) {
-    if (rowb)
-      launch_topk_lanes<true>(a, split, s);
+  p.rowb = a.row_blocks != nullptr;
+  p.sparse = a.sparse != 0;
+  p.split = (!a.sparse && MM3_TOPK_LANES) ? lanes_split(a, rows) : 0;
+  p.rpw = (!p.split && !p.sparse && multi) ? MM3_TOPK_RPW : 1;
+  const int nb = a.nb_max;
+  p.E = nb <= 64 ? 1 : nb <= 128 ? 2 : nb <= 256 ? 4 : nb <= 512 ? 8 : nb <= 1024 ? 16 : 0;
+  return p;
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  const TopkPlan p = plan_topk(a);
+  if (p.split) {
+    if (p.rowb)
+      launch_topk_lanes<true>(a, p.split, s);
     else
-      launch_topk_lanes<false>(a, split, s);
-  } else if (a.sparse)
+      launch_topk_lanes<false>(a, p.split, s);
+  } else if (p.sparse)
     launch_topk_t<true, 1, false>(a, s);
-  else if (multi && rowb)
+  else if (p.rpw > 1 && p.rowb)
     launch_topk_t<false, MM3_TOPK_RPW, true>(a, s);
-  else if (multi)
+  else if (p.rpw > 1)
     launch_topk_t<false, MM3_TOPK_RPW, false>(a, s);
   else
     launch_topk_t<false, 1, false>(a, s);
   return hipGetLastError();
+}
+
+const char* topk_kernel_name(const TopkArgs& a) {
+  const TopkPlan p = plan_topk(a);
+  static thread_local char buf[96];
+  if (p.split)
+    snprintf(buf, sizeof buf, "topk_lanes_kernel<%d, %s, %d>", kLaneChunks, p.rowb ? "true" : "false",
+             p.split);
+  else
+    snprintf(buf, sizeof buf, "topk_kernel<%d, %s, %d, %s>", p.E, p.sparse ? "true" : "false", p.rpw,
+             (p.rpw > 1 && p.rowb) ? "true" : "false");
+  return buf;
 }
 
 // ------------------------------------------------------ sparse block table

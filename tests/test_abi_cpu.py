@@ -331,3 +331,40 @@ BAD_TOPK_BLOCKS = [
 def test_topk_blocks_rules(label, kw, msg):
     assert _topk_blocks(**kw) == B.MM3_EINVAL
     assert msg in _err(), _err()
+
+
+def _selector(s_ptr=FAKE, sh=None, sr=128, sw=128, heads=4, T=32768, msl=16384, topk=16, rowb=0,
+              sparse=0):
+    sh = T * sr if sh is None else sh
+    r = B.lib().mm3_index_topk_selector(s_ptr, sh, sr, sw, heads, T, msl, topk, rowb, sparse)
+    return None if r is None else r.decode()
+
+
+@pytest.mark.parametrize("kw,want", [
+    # chunked-prefill shape: 131072 (row, head) pairs of 128 blocks -> two lanes per row
+    (dict(), "topk_lanes_kernel<4, false, 2>"),
+    (dict(rowb=1), "topk_lanes_kernel<4, true, 2>"),
+    # topk above the lanes' kept list -> several rows per wave, two keys per lane
+    (dict(topk=20), "topk_kernel<2, false, 4, false>"),
+    (dict(topk=20, rowb=1), "topk_kernel<2, false, 4, true>"),
+    # rows past 512 blocks -> the wave-per-row search, 16 keys per lane
+    (dict(msl=70000, sw=560, sr=560), "topk_kernel<16, false, 4, false>"),
+    # a decode batch: one row per wave
+    (dict(heads=4, T=256, msl=32768, sw=256, sr=256), "topk_kernel<4, false, 1, false>"),
+    # the fused sparse table: one head, one row per wave, the sparse form
+    (dict(heads=1, T=1024, msl=131072, sw=1024, sr=1024, sparse=1), "topk_kernel<16, true, 1, false>"),
+    # rows past 1024 blocks re-read the score row
+    (dict(heads=1, T=8, msl=200000, sw=1568, sr=1568), "topk_kernel<0, false, 1, false>"),
+    # unaligned scores cannot take the lanes' 16-byte loads
+    (dict(s_ptr=FAKE + 4), "topk_kernel<2, false, 4, false>"),
+])
+def test_selector_query_names_the_launched_kernel(kw, want):
+    assert _selector(**kw) == want
+
+
+def test_selector_query_rejects_invalid():
+    assert _selector(topk=0) is None
+    assert "topk" in B.lib().mm3_last_error().decode()
+    assert _selector(sw=100) is None  # narrower than cdiv(16384, 128)
+    assert _selector(heads=4, sparse=1) is None
+    assert _selector(msl=65535 * 128) is None

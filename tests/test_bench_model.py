@@ -76,22 +76,31 @@ def test_bench_refuses_several_gpus(monkeypatch, capsys):
 
 
 def test_selector_kernel_follows_the_launch_rule():
-    # the benchmark names the selector kernel the library launches: lanes
-    # selecting rows by themselves for topk <= 16, from 65536, 24576, 16384
-    # or 8192 (head, row) pairs for rows of up to 64, 128, 256 or 512 blocks
-    from types import SimpleNamespace as W
-    lanes = [W(heads=4, rows=32768, topk=16, max_seq_len=16384),     # chunked prefill
-             W(heads=4, rows=8352, topk=16, max_seq_len=32768),      # mixed serving
-             W(heads=4, rows=8192, topk=16, max_seq_len=65536),      # 512 blocks
-             W(heads=4, rows=6144, topk=16, max_seq_len=16384),      # 24576 pairs, 128 blocks
-             W(heads=4, rows=16384, topk=16, max_seq_len=8192)]      # 65536 pairs, 64 blocks
-    ballot = [W(heads=4, rows=256, topk=16, max_seq_len=32768),      # decode batch
-              W(heads=1, rows=512, topk=16, max_seq_len=65536),      # NVFP4 decode
-              W(heads=4, rows=8192, topk=16, max_seq_len=8192),      # 32768 pairs, 64 blocks
-              W(heads=4, rows=4096, topk=16, max_seq_len=16384),     # 16384 pairs, 128 blocks
-              W(heads=4, rows=32768, topk=16, max_seq_len=65537),    # 513 blocks
-              W(heads=4, rows=32768, topk=17, max_seq_len=16384)]    # topk 17
+    # the benchmark names the selector kernel the library itself reports for
+    # the batch (mm3_index_topk_selector): lanes selecting rows by themselves
+    # for topk <= 16, from 65536, 24576, 16384 or 8192 (head, row) pairs for
+    # rows of up to 64, 128, 256 or 512 blocks, else one wave per row
+    from sparse_attention_block_paged_amd import _binding as B
+
+    def name(heads, rows, topk, max_seq_len):
+        w = -(-(-(-max_seq_len // 128)) // 16) * 16
+        r = B.lib().mm3_index_topk_selector(1 << 20, rows * w, w, w, heads, rows, max_seq_len, topk,
+                                            0, 0)
+        return r.decode().split("<")[0]
+
+    lanes = [(4, 32768, 16, 16384),     # chunked prefill
+             (4, 8352, 16, 32768),      # mixed serving
+             (4, 8192, 16, 65536),      # 512 blocks
+             (4, 6144, 16, 16384),      # 24576 pairs, 128 blocks
+             (4, 16384, 16, 8192)]      # 65536 pairs, 64 blocks
+    ballot = [(4, 256, 16, 32768),      # decode batch
+              (1, 512, 16, 65536),      # NVFP4 decode
+              (1, 1024, 16, 131072),    # long decode
+              (4, 8192, 16, 8192),      # 32768 pairs, 64 blocks
+              (4, 4096, 16, 16384),     # 16384 pairs, 128 blocks
+              (4, 32768, 16, 65537),    # 513 blocks
+              (4, 32768, 17, 16384)]    # topk 17
     for w in lanes:
-        assert bench.selector_kernel(w) == "topk_lanes_kernel", w
+        assert name(*w) == "topk_lanes_kernel", w
     for w in ballot:
-        assert bench.selector_kernel(w) == "topk_kernel", w
+        assert name(*w) == "topk_kernel", w

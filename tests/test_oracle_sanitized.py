@@ -44,6 +44,8 @@ CHILD = textwrap.dedent("""
     kd = bf16((pages, 128, 128))
     s, ids = oracle.forward(q, 0, kd, None, bt, lens, Q, 0.0884, 4, 1, 1, W)
     h.update(s.tobytes()); h.update(ids.tobytes())
+    s_b, s64, ids_b = oracle.forward(q, 0, kd, None, bt, lens, Q, 0.0884, 4, 1, 1, W, with64=True)
+    h.update(s_b.tobytes()); h.update(s64.tobytes()); h.update(ids_b.tobytes())
 
     nib = rng.integers(0, 256, (pages, 128, 64), dtype=np.uint8)
     sc = rng.integers(0x20, 0x50, (pages, 128, 8), dtype=np.uint8)

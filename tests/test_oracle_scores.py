@@ -44,11 +44,12 @@ def _keys_f64(a, page_ids):
     return prod.to(torch.float8_e4m3fn).double().numpy()
 
 
-def brute_scores(a, width):
+def brute_scores(a, width, with64=False):
     q = _bf16_to_f64(a["q_bits"])
     T, H, _ = q.shape
     Q = a["query_len"]
     out = np.full((H, T, width), np.nan, dtype=np.float32)
+    out64 = np.full((H, T, width), np.nan, dtype=np.float64)
     for r, L in enumerate(a["seq_lens"]):
         nb = cdiv(int(L), 128)
         if nb == 0:
@@ -63,8 +64,10 @@ def brute_scores(a, width):
             dots = q[t] @ K[: nv * 128].T  # [H, nv*128]
             dots[:, pos + 1:] = -np.inf
             m = dots.reshape(H, nv, 128).max(-1)
+            # sm_scale crosses the boundary as an fp32 value
+            out64[:, t, :nv] = float(np.float32(a["sm_scale"])) * m
             out[:, t, :nv] = (a["sm_scale"] * m).astype(np.float32)
-    return out
+    return (out, out64) if with64 else out
 
 
 def _small(seed, kfmt=KFMT_BF16, R=3, lens=(1, 700), Q=4, H=2, msl=1024, **kw):
@@ -90,6 +93,40 @@ def test_vs_numpy_float64(seed, kfmt):
     w = _small(seed, kfmt=kfmt)
     a = host_arrays(w)
     _same(_oracle_scores(a, w.score_width), brute_scores(a, w.score_width), rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("kfmt", [KFMT_BF16, KFMT_NVFP4])
+def test_scores64_vs_numpy_float64(kfmt):
+    """The oracle's unrounded scores (sm_scale * the fp64 block maximum) equal
+    a numpy float64 matmul's to fp64 summation-order error, and round to the
+    fp32 scores exactly."""
+    w = _small(4, kfmt=kfmt, R=3, lens=(200, 1000))
+    a = host_arrays(w)
+    s64 = np.full((w.heads, w.rows, w.score_width), np.nan)
+    s32 = oracle.block_scores(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"],
+                              a["block_table"], a["seq_lens"], a["query_len"],
+                              a["sm_scale"], w.score_width, out64=s64)
+    _, b64 = brute_scores(a, w.score_width, with64=True)
+    vis = ~np.isnan(b64)
+    assert np.array_equal(vis, ~np.isnan(s64))
+    np.testing.assert_allclose(s64[vis], b64[vis], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(s64[vis].astype(np.float32), s32[vis])
+
+
+def test_scores64_equal_for_copied_keys():
+    """Two blocks holding the same keys, in any slot order, get bit-equal
+    unrounded scores (the tie a checker must treat as exact), while blocks
+    whose fp64 maxima differ get different unrounded scores."""
+    w = _small(8, R=1, lens=(900, 900), Q=4, H=2)
+    bt = w.block_table[0]
+    src = w.kdata[bt[1]].clone()
+    w.kdata[bt[3]] = src.roll(37, dims=0)  # block 3: block 1's keys, rotated
+    a = host_arrays(w)
+    s64 = np.full((w.heads, w.rows, w.score_width), np.nan)
+    oracle.block_scores(a["q_bits"], a["kfmt"], a["kdata"], a["kscales"], a["block_table"],
+                        a["seq_lens"], a["query_len"], a["sm_scale"], w.score_width, out64=s64)
+    assert np.array_equal(s64[:, :, 1], s64[:, :, 3])
+    assert not np.array_equal(s64[:, :, 1], s64[:, :, 2])
 
 
 def test_vs_torch_fp32_special_case():

@@ -11,8 +11,12 @@ from workloads import config, host_arrays
 def case():
     w = config(2, device="cpu", R=4, lens=(300, 3000), max_seq_len=4096)
     a = host_arrays(w)
-    s, ids = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
-    return w, a, s, ids
+    s, s64, ids = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
+    return w, a, s, s64, ids
+
+
+def _ids(w, a, g, ids, s, s64):
+    return P.check_ids(g, ids, s, s64, P.positions_of(a), w.topk, w.init_blocks, w.local_blocks)
 
 
 def _inv(w, a, ids):
@@ -20,10 +24,9 @@ def _inv(w, a, ids):
 
 
 def test_accepts_oracle_output(case):
-    w, a, s, ids = case
+    w, a, s, s64, ids = case
     _inv(w, a, ids)
-    assert P.check_ids(ids, ids, s, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
-                       w.local_blocks) == 0
+    assert _ids(w, a, ids, ids, s, s64) == 0
     assert P.check_scores(s.copy(), s) == 0.0
 
 
@@ -39,7 +42,7 @@ def _row_with_choice(w, a, ids):
 @pytest.mark.parametrize("mistake", ["hole", "unsorted", "dup", "out_of_range", "drop_init",
                                      "drop_local", "swap_worse"])
 def test_planted_id_mistakes_are_caught(case, mistake):
-    w, a, s, ids = case
+    w, a, s, s64, ids = case
     h, t, nv = _row_with_choice(w, a, ids)
     bad = ids.copy()
     row = bad[h, t]
@@ -65,28 +68,84 @@ def test_planted_id_mistakes_are_caught(case, mistake):
         row.sort()
     with pytest.raises(AssertionError):
         _inv(w, a, bad)
-        P.check_ids(bad, ids, s, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
-                    w.local_blocks)
+        _ids(w, a, bad, ids, s, s64)
+
+
+def _boundary(w, ids, s, h, t, nv):
+    """The oracle's k-th (smallest selected non-forced) block and its best
+    unselected one, for row (h, t)."""
+    row = ids[h, t]
+    forced = {0, nv - 1, nv - 2}
+    kth_b = min((b for b in row if b not in forced), key=lambda b: s[h, t, b])
+    out_b = max((b for b in range(nv) if b not in row), key=lambda b: s[h, t, b])
+    return kth_b, out_b
+
+
+def _swap(ids, h, t, a_b, b_b):
+    g = ids.copy()
+    g[h, t, list(g[h, t]).index(a_b)] = b_b
+    g[h, t].sort()
+    return g
 
 
 def test_near_tie_is_accepted(case):
-    w, a, s, ids = case
+    """A block just inside the tolerance of the k-th, with a different
+    unrounded score, may be swapped for it."""
+    w, a, s, s64, ids = case
     h, t, nv = _row_with_choice(w, a, ids)
-    s2 = s.copy()
-    row = ids[h, t]
-    forced = {0, nv - 1, nv - 2}
-    kth_b = min((b for b in row if b not in forced), key=lambda b: s2[h, t, b])
-    out_b = max((b for b in range(nv) if b not in row), key=lambda b: s2[h, t, b])
+    kth_b, out_b = _boundary(w, ids, s, h, t, nv)
+    s2, s64b = s.copy(), s64.copy()
     s2[h, t, out_b] = s2[h, t, kth_b] - 1e-5  # within tolerance below the k-th
-    g = ids.copy()
-    g[h, t, list(row).index(kth_b)] = out_b
-    g[h, t].sort()
-    assert P.check_ids(g, ids, s2, a["seq_lens"], w.query_len, w.topk, w.init_blocks,
+    s64b[h, t, out_b] = s64b[h, t, kth_b] - 1e-5
+    g = _swap(ids, h, t, kth_b, out_b)
+    assert P.check_ids(g, ids, s2, s64b, P.positions_of(a), w.topk, w.init_blocks,
                        w.local_blocks) == 1
 
 
+def test_exact_tie_toward_higher_id_is_caught(case):
+    """Blocks with equal unrounded scores are a true tie: the oracle keeps the
+    lower id, and a GPU row that keeps the higher one fails, even though the
+    score gap (0) is inside the tolerance."""
+    w, a, s, s64, ids = case
+    h, t, nv = _row_with_choice(w, a, ids)
+    kth_b, out_b = _boundary(w, ids, s, h, t, nv)
+    s2, s64b = s.copy(), s64.copy()
+    s2[h, t, out_b] = s2[h, t, kth_b]
+    s64b[h, t, out_b] = s64b[h, t, kth_b]
+    g = _swap(ids, h, t, kth_b, out_b)
+    with pytest.raises(AssertionError, match="exact tie"):
+        P.check_ids(g, ids, s2, s64b, P.positions_of(a), w.topk, w.init_blocks, w.local_blocks)
+    # equal fp32 scores from distinct unrounded values: a near-tie
+    s64b[h, t, out_b] = np.nextafter(s64b[h, t, kth_b], -np.inf)
+    assert P.check_ids(g, ids, s2, s64b, P.positions_of(a), w.topk, w.init_blocks,
+                       w.local_blocks) == 1
+
+
+def test_boundary_ties_counted():
+    """One row, hand-made: 8 visible blocks, topk 4, 1 init + 1 local block;
+    the oracle selects {0, 3, 5, 7}.  With block 2's unrounded score equal to
+    block 3's (the k-th), the boundary is an exact tie; lowered by one ulp,
+    it is not."""
+    s64 = np.array([[[9.0, 1.0, 4.0, 4.0, 2.0, 6.0, 3.0, 0.5]]])
+    ids = np.array([[[0, 3, 5, 7]]], dtype=np.int32)
+    pos = np.array([8 * 128 - 1])
+    # blocks 2 and 3 tie at 4.0; the oracle keeps 2 (the lower id)
+    assert P.boundary_ties(np.array([[[0, 2, 5, 7]]], dtype=np.int32), s64, pos, 4, 1, 1) == 1
+    s64[0, 0, 2] = np.nextafter(4.0, 0.0)
+    assert P.boundary_ties(ids, s64, pos, 4, 1, 1) == 0
+    # fewer visible blocks than topk: no boundary at all
+    assert P.boundary_ties(ids, s64, np.array([3 * 128 - 1]), 4, 1, 1) == 0
+
+
+def test_near_tie_bound_enforced():
+    P.record("bound-ok", 5000, 5, 0)
+    with pytest.raises(AssertionError, match="above the bound"):
+        P.record("bound-exceeded", 5000, 6, 0)
+    del P.LOG[-1:]
+
+
 def test_planted_score_mistakes_are_caught(case):
-    w, a, s, ids = case
+    w, a, s, s64, ids = case
     g = s.copy()
     vis = np.argwhere(~np.isnan(s))
     h, t, b = vis[len(vis) // 2]
@@ -123,7 +182,7 @@ def test_ragged_checkers_catch_a_shifted_position():
     w = make(name="rg", R=3, lens=(700, 3000), Q=300, H=1, max_seq_len=4096, topk=4, I=1, L=1,
              kfmt=0, seed=3, device="cpu", qlens=[2, 300, 5], prefix="tail")
     a = host_arrays(w)
-    s, ids = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
+    s, s64, ids = P.oracle_forward(a, w.score_width, w.topk, w.init_blocks, w.local_blocks)
     P.check_invariants(ids, a["seq_lens"], w.query_len, w.topk, w.init_blocks, w.local_blocks,
                        cu=a["cu_seqlens_q"], prefix=a["prefix_lens"])
     with pytest.raises(AssertionError):
