@@ -258,6 +258,34 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
                      const mm3_sparse_out* sparse, void* stream);
 
 /*
+ * mm3_index_decode_static -- mm3_index_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same computation, arguments and rules
+ * as mm3_index_decode, without the workspace arguments: when scores_out is
+ * NULL the scores go to a workspace the library holds in device memory of
+ * its own, MM3_STATIC_SCRATCH_BYTES (64 MiB) per GPU, allocated when the
+ * library's code is loaded onto the GPU and kept until the process ends.
+ * Nothing is allocated or freed by the call.
+ *   Limit: mm3_index_decode_workspace_bytes(p, topk, 0) at most
+ *   MM3_STATIC_SCRATCH_BYTES (enough for heads * total_q *
+ *   round_up(cdiv(max_seq_len, 128), 16) <= 16 Mi scores, e.g. 4 heads x
+ *   32768 rows x 128 blocks), else MM3_EWORKSPACE and nothing enqueued.
+ *   Sharing: every call on one GPU uses that GPU's one workspace, which
+ *   holds the last call's scores afterwards (nothing in it needs to start
+ *   at zero).  Calls that overlap on one GPU -- on different streams, or
+ *   from different host threads without ordering -- race on it; order them
+ *   on one stream, or give one of them scores_out or mm3_index_decode.
+ */
+#define MM3_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int mm3_index_decode_static(const mm3_problem* p, int32_t topk,
+                            int32_t init_blocks, int32_t local_blocks,
+                            int32_t* out, int64_t o_head_stride,
+                            int64_t o_row_stride, float* scores_out,
+                            int64_t s_head_stride, int64_t s_row_stride,
+                            int32_t s_width, const mm3_sparse_out* sparse,
+                            void* stream);
+
+/*
  * mm3_build_sparse_block_table -- the sparse block table (mm3_sparse_out)
  * of ids already selected, for ONE index head (page "ops.index_topk",
  * minimax_m3_index_decode, the optional table arguments).

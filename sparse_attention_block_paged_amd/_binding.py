@@ -28,9 +28,10 @@ HEAD_DIM = 128
 
 EXPORTED = (
     "mm3_index_score", "mm3_index_topk", "mm3_index_topk_blocks", "mm3_index_decode_workspace_bytes",
-    "mm3_index_decode", "mm3_build_sparse_block_table", "mm3_index_topk_selector",
-    "mm3_last_error", "mm3_version",
+    "mm3_index_decode", "mm3_index_decode_static", "mm3_build_sparse_block_table",
+    "mm3_index_topk_selector", "mm3_last_error", "mm3_version",
 )
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class Mm3Error(RuntimeError):
@@ -109,6 +110,8 @@ def lib():
         L.mm3_index_decode_workspace_bytes.restype = SZ
         L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, PS, P]
         L.mm3_index_decode.restype = ctypes.c_int
+        L.mm3_index_decode_static.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, PS, P]
+        L.mm3_index_decode_static.restype = ctypes.c_int
         L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, PR, PS, P]
         L.mm3_build_sparse_block_table.restype = ctypes.c_int
         L.mm3_index_topk_selector.argtypes = [P, I64, I64, I32, I32, I32, I32, I32, I32, I32]
@@ -352,6 +355,41 @@ def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm
                                   sh, sr, sw, ws_ptr, ws_bytes,
                                   None if sparse is None else ctypes.byref(sparse),
                                   _stream(q, stream)))
+    return out
+
+
+def mm3_index_decode_static(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
+                            topk, init_blocks, local_blocks, out, kscales=None, scores_out=None,
+                            stream=None, cu_seqlens_q=None, prefix_lens=None,
+                            attention_block_table=None, sparse_block_table_out=None,
+                            sparse_context_lens_out=None, pages_per_block=None,
+                            block_page_stride=None):
+    """mm3_index_decode without a workspace argument: the library's own
+    per-GPU score workspace (64 MiB) serves when scores_out is None.  out
+    must be given: nothing here allocates device memory."""
+    sp_args = (attention_block_table, sparse_block_table_out, sparse_context_lens_out,
+               pages_per_block, block_page_stride)
+    if any(x is not None for x in sp_args) and any(x is None for x in sp_args):
+        raise ValueError("sparse-table arguments must be provided together")
+    sparse = None
+    if attention_block_table is not None:
+        sparse = make_sparse_out(attention_block_table, pages_per_block, block_page_stride,
+                                 sparse_block_table_out, sparse_context_lens_out)
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales,
+                     cu_seqlens_q, prefix_lens)
+    if out is None or out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be given: int32 [heads, >=tokens, topk] with unit column stride")
+    if scores_out is not None:
+        if scores_out.dtype != torch.float32 or scores_out.stride(2) != 1:
+            raise ValueError("scores_out must be fp32 with unit column stride")
+        sh, sr, sw = scores_out.stride(0), scores_out.stride(1), scores_out.shape[2]
+    else:
+        sh = sr = sw = 0
+    _check(lib().mm3_index_decode_static(ctypes.byref(p), int(topk), int(init_blocks),
+                                         int(local_blocks), out.data_ptr(), out.stride(0),
+                                         out.stride(1), _ptr(scores_out), sh, sr, sw,
+                                         None if sparse is None else ctypes.byref(sparse),
+                                         _stream(q, stream)))
     return out
 
 

@@ -7,12 +7,19 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "mm3_index.h"
 #include "mm3_launch.h"
 
 using namespace mm3;
+
+// Score workspace of mm3_index_decode_static: device memory the library owns,
+// one copy per GPU (zero at load; held until the process ends).  Host code
+// never uses this name as an address: scratch_ptr() looks the copy of the
+// current device up once and passes that address on.
+static __device__ __align__(256) uint8_t scratch[MM3_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -273,6 +280,26 @@ TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t sw, int32_t h
 
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// The device address of `scratch` on the current device, looked up the
+// first time a device asks (with that device current) and kept per device.
+// Returns nullptr after setting the error message when the lookup fails.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice"), nullptr;
+  if (dev < 0 || dev >= 64) return fail(MM3_EHIP, "device index %d out of range", dev), nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)"), nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -443,6 +470,34 @@ const char* mm3_index_topk_selector(const float* scores, int64_t s_head_stride, 
   a.s_bytes = score_bytes(s_head_stride, s_row_stride, s_width, heads, total_q);
   g_err.clear();
   return topk_kernel_name(a);
+}
+
+int mm3_index_decode_static(const mm3_problem* p, int32_t topk, int32_t init_blocks,
+                            int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                            int64_t o_row_stride, float* scores_out, int64_t s_head_stride,
+                            int64_t s_row_stride, int32_t s_width, const mm3_sparse_out* sparse,
+                            void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (!scores_out) {
+    const size_t need = mm3_index_decode_workspace_bytes(p, topk, 0);
+    if (need > MM3_STATIC_SCRATCH_BYTES)
+      return fail(MM3_EWORKSPACE,
+                  "the scores of this batch need %zu bytes of workspace, more than the %zu the "
+                  "library holds for mm3_index_decode_static; pass scores_out or call "
+                  "mm3_index_decode with a workspace",
+                  need, (size_t)MM3_STATIC_SCRATCH_BYTES);
+    if (need) {
+      if (!(ws = scratch_ptr())) return MM3_EHIP;
+      ws_bytes = MM3_STATIC_SCRATCH_BYTES;
+    }
+  }
+  return mm3_index_decode(p, topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride,
+                          scores_out, s_head_stride, s_row_stride, s_width, ws, ws_bytes, sparse,
+                          stream);
 }
 
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, int32_t topk,

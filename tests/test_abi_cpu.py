@@ -368,3 +368,22 @@ def test_selector_query_rejects_invalid():
     assert _selector(sw=100) is None  # narrower than cdiv(16384, 128)
     assert _selector(heads=4, sparse=1) is None
     assert _selector(msl=65535 * 128) is None
+
+
+def test_static_decode_validates_before_any_hip_call():
+    """The no-allocation decode checks its arguments, and that the batch's
+    scores fit the library's 64 MiB workspace, before touching the GPU."""
+    lib = B.lib()
+    out = ctypes.c_void_p(FAKE * 5)
+    # 4 heads x 32800 rows x 128 blocks of scores: past 64 MiB
+    p = _problem(heads=4, num_reqs=4, query_len=8200, max_seq_len=16384, bt_width=128,
+                 bt_row_stride=128)
+    rc = lib.mm3_index_decode_static(ctypes.byref(p), 16, 1, 2, out, 32800 * 16, 16, None, 0, 0, 0,
+                                     None, None)
+    assert rc == B.MM3_EWORKSPACE
+    msg = lib.mm3_last_error().decode()
+    assert "67174400" in msg and str(B.STATIC_SCRATCH_BYTES) in msg
+    p = _problem(heads=4)
+    rc = lib.mm3_index_decode_static(ctypes.byref(p), 0, 0, 0, out, 32 * 16, 16, None, 0, 0, 0,
+                                     None, None)
+    assert rc == B.MM3_EINVAL and "topk" in lib.mm3_last_error().decode()
