@@ -262,6 +262,27 @@ def measure(cid, torch, dev, steps, warmup, ncopies, graph=False, detail=True, k
         torch.cuda.synchronize()
         ms_graph = timed(lambda i: graphs[i % len(graphs)].replay(), steps, warmup)
 
+    # the prefill scorer with the selection fused in (a separate entry point,
+    # measured slower than the step above on these shapes): its step time
+    ms_fused = None
+    if prefill and not base.ragged:
+        fws = []
+        for w in copies:
+            p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                 w.max_seq_len, w.sm_scale, w.kscales)
+            fws.append(torch.empty(mm3.prefill_select_workspace_bytes(p, w.topk, False),
+                                   dtype=torch.uint8, device=dev))
+
+        def fused_step(i):
+            c = i % len(copies)
+            w = copies[c]
+            mm3.mm3_index_prefill_select(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                         w.max_seq_len, w.sm_scale, w.topk, w.init_blocks,
+                                         w.local_blocks, kscales=w.kscales, out=outs[c],
+                                         workspace=fws[c])
+        ms_fused = timed(fused_step, steps, warmup)
+        del fws
+
     # kernels alone, on the same stream (HIP events), same inputs
     n_k = max(steps, 20)
     ms_score = timed(score_only, n_k, 3)
@@ -314,6 +335,7 @@ def measure(cid, torch, dev, steps, warmup, ncopies, graph=False, detail=True, k
                                                           base.topk),
                       ms=round(ms_topk, 4), achieved_gbs=round(sel_gbs, 1),
                       bytes=alg["selector_bytes"]),
+        fused_prefill_select_ms=None if ms_fused is None else round(ms_fused, 4),
         scorer_ms_p10_p50_p90=pct_score,
         scorer_ms_warm=None if ms_score_warm is None else round(ms_score_warm, 4),
         prefill=prefill, tokens=alg["tokens"], rows=alg["rows"],
@@ -352,6 +374,8 @@ def extra_line(res):
          "selector": {k: res["selector"][k] for k in ("kernel", "ms")}}
     if res["step_frac"] is not None:
         e["step_frac_hbm"] = res["step_frac"]
+    if res["fused_prefill_select_ms"] is not None:
+        e["fused_prefill_select_ms"] = res["fused_prefill_select_ms"]
     if res["config_id"] == 1:
         e["us_per_step"] = round(res["ms_per_step"] * 1e3, 2)
         e["note"] = "latency only: 8 blocks of keys, too small for a roofline figure"
@@ -434,6 +458,7 @@ def main():
         "step_frac_hbm": res["step_frac"],
         "selector": res["selector"],
         "step_ms_graph": None if res["ms_graph"] is None else round(res["ms_graph"], 5),
+        "fused_prefill_select_ms": res["fused_prefill_select_ms"],
         "step_ms_p10_p50_p90": res["step_ms_p10_p50_p90"],
         "scorer_ms_p10_p50_p90": res["scorer_ms_p10_p50_p90"],
         "scorer_ms_warm": res["scorer_ms_warm"],

@@ -57,7 +57,7 @@ extern "C" {
 /* return codes */
 #define MM3_OK 0
 #define MM3_EINVAL (-1)       /* an argument breaks a rule listed below */
-#define MM3_EUNSUPPORTED (-2) /* valid, but not implemented (reserved; no call returns it now) */
+#define MM3_EUNSUPPORTED (-2) /* valid, but outside what the call supports */
 #define MM3_EWORKSPACE (-3)   /* workspace NULL, misaligned or too small */
 #define MM3_EHIP (-4)         /* a HIP launch failed; message has the HIP error */
 
@@ -256,6 +256,34 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
                      int64_t s_head_stride, int64_t s_row_stride,
                      int32_t s_width, void* workspace, size_t workspace_bytes,
                      const mm3_sparse_out* sparse, void* stream);
+
+/*
+ * mm3_index_prefill_select -- the prefill scorer with the selection fused in
+ * (page "ops.index_topk": minimax_m3_index_score followed by
+ * minimax_m3_index_topk, in one scorer pass): the workgroup that completes a
+ * 512-row tile's blocks selects the tile's rows itself, with no separate
+ * selector launch.  Arguments, outputs and rules as in mm3_index_decode
+ * (without the sparse table).  Measured slower than mm3_index_decode on the
+ * chunked-prefill shapes -- the tiles complete at the end of the scorer's
+ * shares, where one workgroup per tile selects with far less parallelism
+ * than the selector launch -- so it is a separate call, not a default.
+ *   Batches: uniform (no cu_seqlens_q) with heads * query_len > 16, topk <=
+ *   16, cdiv(max_seq_len, 128) <= 512, at most 65536 (request, 512-row tile)
+ *   units, and scores 16-byte aligned with row and head strides multiples
+ *   of 4 (the workspace's scores are); others get MM3_EUNSUPPORTED.
+ *   workspace   device memory of >= mm3_index_prefill_select_workspace_bytes(),
+ *               256-byte aligned, required (it holds per-tile counters even
+ *               with scores_out); its contents need no initialisation (the
+ *               call resets the counters); overlapping calls must not share it.
+ */
+size_t mm3_index_prefill_select_workspace_bytes(const mm3_problem* p, int32_t topk,
+                                                int32_t with_scores_out);
+int mm3_index_prefill_select(const mm3_problem* p, int32_t topk, int32_t init_blocks,
+                             int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                             int64_t o_row_stride, float* scores_out,
+                             int64_t s_head_stride, int64_t s_row_stride,
+                             int32_t s_width, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * mm3_index_decode_static -- mm3_index_decode for callers that cannot

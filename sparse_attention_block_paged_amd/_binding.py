@@ -28,7 +28,8 @@ HEAD_DIM = 128
 
 EXPORTED = (
     "mm3_index_score", "mm3_index_topk", "mm3_index_topk_blocks", "mm3_index_decode_workspace_bytes",
-    "mm3_index_decode", "mm3_index_decode_static", "mm3_build_sparse_block_table",
+    "mm3_index_decode", "mm3_index_decode_static", "mm3_index_prefill_select",
+    "mm3_index_prefill_select_workspace_bytes", "mm3_build_sparse_block_table",
     "mm3_index_topk_selector", "mm3_last_error", "mm3_version",
 )
 STATIC_SCRATCH_BYTES = 64 << 20
@@ -110,6 +111,10 @@ def lib():
         L.mm3_index_decode_workspace_bytes.restype = SZ
         L.mm3_index_decode.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, PS, P]
         L.mm3_index_decode.restype = ctypes.c_int
+        L.mm3_index_prefill_select_workspace_bytes.argtypes = [PP, I32, I32]
+        L.mm3_index_prefill_select_workspace_bytes.restype = SZ
+        L.mm3_index_prefill_select.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, P, SZ, P]
+        L.mm3_index_prefill_select.restype = ctypes.c_int
         L.mm3_index_decode_static.argtypes = [PP, I32, I32, I32, P, I64, I64, P, I64, I64, I32, PS, P]
         L.mm3_index_decode_static.restype = ctypes.c_int
         L.mm3_build_sparse_block_table.argtypes = [P, I64, I32, PR, PS, P]
@@ -355,6 +360,43 @@ def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm
                                   sh, sr, sw, ws_ptr, ws_bytes,
                                   None if sparse is None else ctypes.byref(sparse),
                                   _stream(q, stream)))
+    return out
+
+
+def prefill_select_workspace_bytes(p: Problem, topk: int, with_scores_out: bool) -> int:
+    n = lib().mm3_index_prefill_select_workspace_bytes(ctypes.byref(p), int(topk),
+                                                       int(with_scores_out))
+    if n == 0:
+        raise Mm3Error(MM3_EUNSUPPORTED, lib().mm3_last_error().decode())
+    return n
+
+
+def mm3_index_prefill_select(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
+                             topk, init_blocks, local_blocks, kscales=None, out=None,
+                             scores_out=None, workspace=None, stream=None):
+    """The prefill scorer with the selection fused in (uniform prefill-shaped
+    batches); returns out [heads, tokens, topk] int32."""
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales)
+    H, T = q.shape[1], q.shape[0]
+    if out is None:
+        out = torch.empty((H, T, topk), dtype=torch.int32, device=q.device)
+    if out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1:
+        raise ValueError("out must be int32 [heads, >=tokens, topk] with unit column stride")
+    if workspace is None:
+        workspace = torch.empty(prefill_select_workspace_bytes(p, topk, scores_out is not None),
+                                dtype=torch.uint8, device=q.device)
+    if scores_out is not None:
+        if scores_out.dtype != torch.float32 or scores_out.stride(2) != 1:
+            raise ValueError("scores_out must be fp32 with unit column stride")
+        sh, sr, sw = scores_out.stride(0), scores_out.stride(1), scores_out.shape[2]
+    else:
+        sh = sr = sw = 0
+    _check(lib().mm3_index_prefill_select(ctypes.byref(p), int(topk), int(init_blocks),
+                                          int(local_blocks), out.data_ptr(), out.stride(0),
+                                          out.stride(1), _ptr(scores_out), sh, sr, sw,
+                                          workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(q, stream)))
     return out
 
 

@@ -28,6 +28,11 @@ HIP_FLAGS = [
 # they take ~8% of the vector instructions out of the NVFP4 scorer's loop.
 SOURCE_FLAGS = {
     "decode_score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # prefill_score: its page copies set M0 in inline assembly, so no
+    # compiler-generated code there may read M0; the wave-level combining of
+    # the fused selection's counter atomics would (v_writelane with an M0
+    # lane index), so atomics are left as written
+    "prefill_score.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 
 

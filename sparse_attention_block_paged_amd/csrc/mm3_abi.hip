@@ -280,6 +280,31 @@ TopkArgs topk_args(const float* s, int64_t sh, int64_t sr, int32_t sw, int32_t h
 
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// Bytes of the decode workspace's score area (0 with scores_out).
+size_t workspace_score_bytes(const mm3_problem* p, int32_t with_scores_out) {
+  if (with_scores_out) return 0;
+  const int64_t T = p->rows.total_q;
+  const int64_t width = cdiv64(cdiv64(p->rows.max_seq_len, MM3_BLOCK), 16) * 16;
+  return round256((size_t)(p->heads * T * width) * sizeof(float));
+}
+
+// int32 words the fused prefill selection needs after the score area (a
+// counter and an owner per row tile), or 0 when the batch cannot take it:
+// uniform batches whose requests all go to the prefill scorer, no sparse
+// table, a selection the lane selector takes (the score layout is checked
+// at the call).
+int fused_prefill_counters(const mm3_problem* p, int32_t topk, const mm3_sparse_out* sparse) {
+  if (sparse || p->rows.cu_seqlens_q || p->rows.total_q == 0 || p->rows.max_seq_len == 0 ||
+      (int64_t)p->heads * p->rows.query_len <= kDecodeRows)
+    return 0;
+  ScoreArgs sa = score_args(p, nullptr, 0, 0);
+  TopkArgs sel{};
+  sel.topk = topk;
+  sel.heads = p->heads;
+  sel.s_bytes = 1;
+  return prefill_select_counters(sa, sel);
+}
+
 // The device address of `scratch` on the current device, looked up the
 // first time a device asks (with that device current) and kept per device.
 // Returns nullptr after setting the error message when the lookup fails.
@@ -306,7 +331,7 @@ extern "C" {
 
 const char* mm3_last_error(void) { return g_err.c_str(); }
 
-const char* mm3_version(void) { return "mm3idx 0.1 gfx950"; }
+const char* mm3_version(void) { return "mm3idx 0.2 gfx950"; }
 
 int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
                     int64_t s_row_stride, int32_t s_width, void* stream) {
@@ -395,10 +420,21 @@ size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk, int3
   if (check_problem(p)) return 0;
   if (check_select(topk, 0, 0)) return 0;
   g_err.clear();
-  if (with_scores_out) return 0;
-  const int64_t T = p->rows.total_q;
-  const int64_t width = cdiv64(cdiv64(p->rows.max_seq_len, MM3_BLOCK), 16) * 16;
-  return round256((size_t)(p->heads * T * width) * sizeof(float));
+  return workspace_score_bytes(p, with_scores_out);
+}
+
+size_t mm3_index_prefill_select_workspace_bytes(const mm3_problem* p, int32_t topk, int32_t with_scores_out) {
+  if (check_problem(p)) return 0;
+  if (check_select(topk, 0, 0)) return 0;
+  const int nctr = fused_prefill_counters(p, topk, nullptr);
+  if (nctr == 0) {
+    fail(MM3_EUNSUPPORTED, "the batch cannot take the fused prefill selection (it needs a uniform batch "
+                           "whose requests all go to the prefill scorer, topk <= 16, rows of at most 512 "
+                           "blocks and at most 65536 row tiles)");
+    return 0;
+  }
+  g_err.clear();
+  return workspace_score_bytes(p, with_scores_out) + round256((size_t)nctr * sizeof(int32_t));
 }
 
 int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
@@ -415,13 +451,13 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   float* s = scores_out;
   int64_t sh = s_head_stride, sr = s_row_stride;
   int32_t sw = s_width;
+  const size_t score_area = workspace_score_bytes(p, s != nullptr);
   if (s) {
     if ((rc = check_scores(p, s, sh, sr, sw))) return rc;
   } else {
-    const size_t need = mm3_index_decode_workspace_bytes(p, topk, 0);
-    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    if (score_area && (!workspace || workspace_bytes < score_area || !aligned(workspace, 256)))
       return fail(MM3_EWORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes (got %zu)",
-                  need, workspace_bytes);
+                  mm3_index_decode_workspace_bytes(p, topk, 0), workspace_bytes);
     sw = (int32_t)(cdiv64(cdiv64(p->rows.max_seq_len, MM3_BLOCK), 16) * 16);
     sr = sw;
     sh = T * sr;
@@ -429,13 +465,13 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   }
   if (T == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
-  if (p->rows.max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
   TopkArgs a = topk_args(s, sh, sr, sw, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
                          o_head_stride, o_row_stride);
   if (sparse) {
     a.sp = sparse_of(sparse);
     a.sparse = 1;
   }
+  if (p->rows.max_seq_len > 0 && (rc = launch_scores(p, s, sh, sr, st))) return rc;
   hipError_t e = launch_topk(a, st);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
@@ -472,6 +508,47 @@ const char* mm3_index_topk_selector(const float* scores, int64_t s_head_stride, 
   return topk_kernel_name(a);
 }
 
+int mm3_index_prefill_select(const mm3_problem* p, int32_t topk, int32_t init_blocks,
+                             int32_t local_blocks, int32_t* out, int64_t o_head_stride,
+                             int64_t o_row_stride, float* scores_out, int64_t s_head_stride,
+                             int64_t s_row_stride, int32_t s_width, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
+  const int64_t T = p->rows.total_q;
+  if ((rc = check_out(out, o_head_stride, o_row_stride, p->heads, T, topk))) return rc;
+  const int nctr = fused_prefill_counters(p, topk, nullptr);
+  if (nctr == 0)
+    return fail(MM3_EUNSUPPORTED, "the batch cannot take the fused prefill selection (it needs a uniform "
+                                  "batch whose requests all go to the prefill scorer, topk <= 16, rows of at "
+                                  "most 512 blocks and at most 65536 row tiles)");
+  float* s = scores_out;
+  int64_t sh = s_head_stride, sr = s_row_stride;
+  int32_t sw = s_width;
+  const size_t score_area = workspace_score_bytes(p, s != nullptr);
+  const size_t need = score_area + round256((size_t)nctr * sizeof(int32_t));
+  if (s && (rc = check_scores(p, s, sh, sr, sw))) return rc;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(MM3_EWORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes (got %zu)", need,
+                workspace_bytes);
+  if (!s) {
+    sw = (int32_t)(cdiv64(cdiv64(p->rows.max_seq_len, MM3_BLOCK), 16) * 16);
+    sr = sw;
+    sh = T * sr;
+    s = static_cast<float*>(workspace);
+  }
+  TopkArgs a = topk_args(s, sh, sr, sw, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
+                         o_head_stride, o_row_stride);
+  if (!lanes_layout_ok(a))
+    return fail(MM3_EUNSUPPORTED, "the fused prefill selection reads score rows 16 bytes at a time: scores "
+                                  "16-byte aligned, row and head strides multiples of 4, under 2 GiB");
+  int32_t* ctr = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + score_area);
+  hipError_t e = launch_prefill_score_select(score_args(p, s, sh, sr), p->kfmt, a, ctr, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fused scorer launch");
+  return ok();
+}
+
 int mm3_index_decode_static(const mm3_problem* p, int32_t topk, int32_t init_blocks,
                             int32_t local_blocks, int32_t* out, int64_t o_head_stride,
                             int64_t o_row_stride, float* scores_out, int64_t s_head_stride,
@@ -483,17 +560,15 @@ int mm3_index_decode_static(const mm3_problem* p, int32_t topk, int32_t init_blo
   void* ws = nullptr;
   size_t ws_bytes = 0;
   if (!scores_out) {
-    const size_t need = mm3_index_decode_workspace_bytes(p, topk, 0);
+    const size_t need = workspace_score_bytes(p, 0);
     if (need > MM3_STATIC_SCRATCH_BYTES)
       return fail(MM3_EWORKSPACE,
                   "the scores of this batch need %zu bytes of workspace, more than the %zu the "
                   "library holds for mm3_index_decode_static; pass scores_out or call "
                   "mm3_index_decode with a workspace",
                   need, (size_t)MM3_STATIC_SCRATCH_BYTES);
-    if (need) {
-      if (!(ws = scratch_ptr())) return MM3_EHIP;
-      ws_bytes = MM3_STATIC_SCRATCH_BYTES;
-    }
+    if (!(ws = scratch_ptr())) return MM3_EHIP;
+    ws_bytes = MM3_STATIC_SCRATCH_BYTES;
   }
   return mm3_index_decode(p, topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride,
                           scores_out, s_head_stride, s_row_stride, s_width, ws, ws_bytes, sparse,

@@ -94,6 +94,17 @@ hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_prefill_score_nvfp4(const ScoreArgs& a, hipStream_t s);
+// The prefill scorer with the selection fused in (every request of the batch
+// must go to the prefill scorer).  prefill_select_counters: the int32
+// words of device memory (any contents; the launch resets them) the fused
+// launch needs -- a counter and an owner per row tile -- or 0 when the batch
+// cannot take it (topk above 16, rows past 512 blocks, more row tiles than
+// the balanced grid takes, a score layout the lane selector cannot read).
+int prefill_select_counters(const ScoreArgs& a, const TopkArgs& sel);
+hipError_t launch_prefill_score_select(const ScoreArgs& a, int kfmt, const TopkArgs& sel, int32_t* ctr,
+                                       hipStream_t s);
+// Whether a score tensor's layout suits the lane selector's 16-byte row loads.
+bool lanes_layout_ok(const TopkArgs& a);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // The selector kernel launch_topk runs for these arguments, as its name and
 // template arguments (host only; the string lives until the thread's next call).

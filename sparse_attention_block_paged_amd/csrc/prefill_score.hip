@@ -35,10 +35,23 @@
 // Two workgroups (80 KiB of LDS each) share a CU, so one's barrier or copy
 // wait is covered by the other's multiplies; wave priorities that fall with
 // the progress through a share keep the two abreast to the end.
+//
+// Fused selection (SEL > 0; page "ops.index_topk": minimax_m3_index_score
+// followed by minimax_m3_index_topk, here in one launch).  A row tile's
+// steps are split between the shares of two or three workgroups.  When a
+// wave finishes its part of a tile it publishes its score stores (release at
+// device scope) and adds its step count to the tile's counter; the wave whose
+// count completes the tile (every wave of every part: waves x steps) records
+// its workgroup as the tile's owner.  After its share, each workgroup
+// selects the rows of the tiles it owns with the lane selector (SEL lanes
+// per row), in its then idle LDS.  No workgroup ever waits for another, and
+// the selection stays out of the multiply loop and its registers.  Counters
+// and owners are reset by a small kernel launched just before.
 #include <atomic>
 
 #include "mm3_device.h"
 #include "mm3_fp4.h"
+#include "mm3_lanes.h"
 #include "mm3_launch.h"
 #include "mm3_rows.h"
 
@@ -144,8 +157,9 @@ struct PfCursor {
   int u, r, x, p0, n, row0, nv, b;
 };
 
-template <int KFMT, bool BALANCED>
-__global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(ScoreArgs a, int units, int tiles) {
+template <int KFMT, bool BALANCED, int SEL>
+__global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(ScoreArgs a, int units, int tiles,
+                                                                              TopkArgs sel, int32_t* ctr) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLdsOf<KFMT>];
   // bf16: two page buffers.  NVFP4: one decoded page buffer plus two staging
   // slots for the raw page.
@@ -455,6 +469,46 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
     }
   };
 
+  // ---- fused selection.  ctr[u]: steps of tile u scored so far, counted
+  // per wave; ctr[units + u]: the workgroup that completed it (-1 before).
+  // A wave at the end of its part of tile cur.u (`done` steps).
+  auto tile_part_done = [&](int done) __attribute__((always_inline)) {
+    // this wave's score stores become visible device-wide before the count
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr + cur.u, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old + done == kPfWaves * cur.nv && lane == 0)
+      __hip_atomic_store(ctr + units + cur.u, (int)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // After the share: select the rows of the tiles in [u_first, u_last] this
+  // workgroup owns, with the page buffers as the waves' scratch.
+  auto select_owned = [&](int u_first, int u_last) __attribute__((always_inline)) {
+    constexpr int kSplit = SEL > 0 ? SEL : 1;  // (SEL == 0 never calls this)
+    wait_vmcnt<0>();  // this wave's owner stores are complete
+    __syncthreads();  // ... and every wave's; the LDS is idle
+    float* const trw = reinterpret_cast<float*>(smem) + wave * (64 * kLaneRowFloats);
+    for (int u = u_first; u <= u_last; ++u) {
+      const int owner = __hip_atomic_load(ctr + units + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readfirstlane(owner) != (int)blockIdx.x) continue;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other parts' score stores
+      PfCursor t;
+      unit_at(t, u);
+      // the tile's flattened rows [i0, i1): position j = i / H, head h =
+      // i % H; per head, one lane-selector pass per 64 / SEL consecutive
+      // rows, the passes dealt round-robin to the waves
+      const int i0 = t.x * kPrefillRows, i1 = min(H * t.n, i0 + kPrefillRows);
+      int pass = 0;
+      for (int h = 0; h < H; ++h) {
+        const int jlo = (i0 - h + H - 1) / H;                         // first j with j H + h >= i0
+        const int jend = i1 - 1 - h >= 0 ? (i1 - 1 - h) / H + 1 : 0;  // past the last
+        for (int j = jlo; j < jend; j += 64 / kSplit, ++pass)
+          if (pass % kPfWaves == wave)
+            lane_select<kLaneChunks, false, kSplit>(sel, h, t.row0 + j, t.row0 + jend, trw);
+      }
+    }
+  };
+
   // ---- the ring: block of step i sits in buffer i & 1; the copy of step
   // i + 1 is started once every wave is past step i - 1.
   if constexpr (KFMT == 1) {
@@ -466,7 +520,8 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
     copy_page(kbuf0, nxt);
   else
     copy_fp4(0, nxt);
-  int bfirst = cur.b, nst = 0;
+  int bfirst = cur.b, nst = 0, tile_done = 0;
+  const int u_first = cur.u;
   for (int i = 0; i < nsteps; ++i) {
     uint8_t* const kl = (KFMT == 0 && (i & 1)) ? kbuf1 : kbuf0;
     ring_sync();
@@ -503,23 +558,68 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
     ++nst;
     const bool last = i + 1 == nsteps;
     const bool tile_end = cur.b + 1 == cur.nv;
-    if (nst == kPfStage || tile_end || last) {
-      flush(bfirst, nst);
-      nst = 0;
-      bfirst = cur.b + 1;
-    }
-    if (!last) {
-      advance(cur);
-      if (cur.b == 0) {
-        bfirst = 0;
-        load_q();
+    if constexpr (SEL == 0) {
+      if (nst == kPfStage || tile_end || last) {
+        flush(bfirst, nst);
+        nst = 0;
+        bfirst = cur.b + 1;
       }
+      if (!last) {
+        advance(cur);
+        if (cur.b == 0) {
+          bfirst = 0;
+          load_q();
+        }
+      }
+    } else {
+      ++tile_done;
+      if (nst == kPfStage || tile_end || last) {
+        flush(bfirst, nst);
+        nst = 0;
+        bfirst = cur.b + 1;
+      }
+      if (tile_end || last) {
+        tile_part_done(tile_done);
+        tile_done = 0;
+      }
+      if (!last) {
+        advance(cur);
+        if (cur.b == 0) {
+          bfirst = 0;
+          load_q();
+        }
+      }
+    }
+  }
+  if constexpr (SEL > 0) select_owned(u_first, cur.u);
+}
+
+// Ahead of the fused scorer: resets the tile counters (0) and owners (-1)
+// -- ctr holds 2 * units words -- and writes the ids of the tiles that have
+// no steps (rows that all sit before position 0 see no block: all -1), which
+// no workgroup completes.  One wave per unit.
+__global__ __launch_bounds__(256) void fused_reset_kernel(int32_t* ctr, int units, int tiles, ScoreArgs a,
+                                                          TopkArgs sel) {
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  for (int i = gt; i < 2 * units; i += gridDim.x * 256) ctr[i] = i < units ? 0 : -1;
+  const int lane = threadIdx.x & 63;
+  const int H = a.heads;
+  for (int u = gt >> 6; u < units; u += gridDim.x * 4) {
+    const int r = u / tiles, x = u - r * tiles;
+    const ReqRows q = req_rows(a.rows, r);
+    if (x * kPrefillRows >= H * q.n || tile_blocks(q.p0, q.n, x, H) > 0) continue;
+    const int i0 = x * kPrefillRows, i1 = min(H * q.n, i0 + kPrefillRows);
+    for (int e = lane; e < (i1 - i0) * sel.topk; e += 64) {
+      const int i = i0 + e / sel.topk, k = e - (e / sel.topk) * sel.topk;
+      const int j = i / H, h = i - j * H;
+      sel.out[(int64_t)h * sel.o_head + (int64_t)(q.row0 + j) * sel.o_row + k] = -1;
     }
   }
 }
 
-// Persistent grid: workgroups that fit the chip at once, cached per device.
-template <int KFMT>
+// Persistent grid: workgroups that fit the chip at once, cached per device
+// and kernel.
+template <int KFMT, int SEL>
 static int prefill_grid() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -527,8 +627,8 @@ static int prefill_grid() {
   int g = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (g <= 0) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_score_kernel<KFMT, true>, kPfThreads, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_score_kernel<KFMT, true, SEL>, kPfThreads,
+                                                     0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     g = device_cus() * per_cu;
@@ -537,17 +637,37 @@ static int prefill_grid() {
   return g;
 }
 
+// (request, row tile) units of a batch: the tiles a request of up to
+// query_len rows has, for every request.
+static int64_t prefill_units(const ScoreArgs& a, int* tiles) {
+  *tiles = (a.heads * a.rows.qlen + kPrefillRows - 1) / kPrefillRows;  // per request, at most
+  return (int64_t)a.rows.num_reqs * *tiles;
+}
+
+static bool prefill_balanced(const ScoreArgs& a) {
+  int tiles = 0;
+  const int64_t units = prefill_units(a, &tiles);
+  // the scan counts steps in 32-bit integers
+  return units <= kPfBalancedMaxUnits && units * a.nb_max <= INT32_MAX;
+}
+
+template <int KFMT, int SEL>
+static void launch_prefill_t(const ScoreArgs& a, const TopkArgs& sel, int32_t* ctr, hipStream_t s) {
+  int tiles = 0;
+  const int units = (int)prefill_units(a, &tiles);
+  hipLaunchKernelGGL((prefill_score_kernel<KFMT, true, SEL>), dim3(prefill_grid<KFMT, SEL>()), dim3(kPfThreads), 0,
+                     s, a, units, tiles, sel, ctr);
+}
+
 template <int KFMT>
 static hipError_t launch_prefill(const ScoreArgs& a, hipStream_t s) {
-  const int tiles = (a.heads * a.rows.qlen + kPrefillRows - 1) / kPrefillRows;  // per request, at most
-  const int64_t units = (int64_t)a.rows.num_reqs * tiles;
-  // the scan counts steps in 32-bit integers
-  if (units <= kPfBalancedMaxUnits && units * a.nb_max <= INT32_MAX) {
-    hipLaunchKernelGGL((prefill_score_kernel<KFMT, true>), dim3(prefill_grid<KFMT>()), dim3(kPfThreads), 0, s, a,
-                       (int)units, tiles);
+  int tiles = 0;
+  const int64_t units = prefill_units(a, &tiles);
+  if (prefill_balanced(a)) {
+    launch_prefill_t<KFMT, 0>(a, TopkArgs{}, nullptr, s);
   } else {
-    hipLaunchKernelGGL((prefill_score_kernel<KFMT, false>), dim3((unsigned)units), dim3(kPfThreads), 0, s, a,
-                       (int)units, tiles);
+    hipLaunchKernelGGL((prefill_score_kernel<KFMT, false, 0>), dim3((unsigned)units), dim3(kPfThreads), 0, s, a,
+                       (int)units, tiles, TopkArgs{}, (int32_t*)nullptr);
   }
   return hipGetLastError();
 }
@@ -555,5 +675,31 @@ static hipError_t launch_prefill(const ScoreArgs& a, hipStream_t s) {
 hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s) { return launch_prefill<0>(a, s); }
 
 hipError_t launch_prefill_score_nvfp4(const ScoreArgs& a, hipStream_t s) { return launch_prefill<1>(a, s); }
+
+int prefill_select_counters(const ScoreArgs& a, const TopkArgs& sel) {
+  if (sel.topk > kLaneTop || a.nb_max > 16 * kLaneChunks * 8 || !prefill_balanced(a) || !lanes_layout_ok(sel))
+    return 0;
+  int tiles = 0;
+  return 2 * (int)prefill_units(a, &tiles);
+}
+
+hipError_t launch_prefill_score_select(const ScoreArgs& a, int kfmt, const TopkArgs& sel, int32_t* ctr,
+                                       hipStream_t s) {
+  int tiles = 0;
+  const int units = (int)prefill_units(a, &tiles);
+  hipLaunchKernelGGL(fused_reset_kernel, dim3(min(1024, (units + 3) / 4)), dim3(256), 0, s, ctr, units, tiles, a,
+                     sel);
+  int split = 1;
+  while (16 * kLaneChunks * split < a.nb_max) split *= 2;
+  const bool nv4 = kfmt == 1;
+  switch (split) {
+    case 1: nv4 ? launch_prefill_t<1, 1>(a, sel, ctr, s) : launch_prefill_t<0, 1>(a, sel, ctr, s); break;
+    case 2: nv4 ? launch_prefill_t<1, 2>(a, sel, ctr, s) : launch_prefill_t<0, 2>(a, sel, ctr, s); break;
+    case 4: nv4 ? launch_prefill_t<1, 4>(a, sel, ctr, s) : launch_prefill_t<0, 4>(a, sel, ctr, s); break;
+    case 8: nv4 ? launch_prefill_t<1, 8>(a, sel, ctr, s) : launch_prefill_t<0, 8>(a, sel, ctr, s); break;
+    default: return hipErrorInvalidValue;  // prefill_select_counters admits no such batch
+  }
+  return hipGetLastError();
+}
 
 }  // namespace mm3

@@ -387,3 +387,33 @@ def test_static_decode_validates_before_any_hip_call():
     rc = lib.mm3_index_decode_static(ctypes.byref(p), 0, 0, 0, out, 32 * 16, 16, None, 0, 0, 0,
                                      None, None)
     assert rc == B.MM3_EINVAL and "topk" in lib.mm3_last_error().decode()
+
+
+def test_fused_prefill_workspace_sizes():
+    """The fused prefill selection asks for two int32 words per (request,
+    512-row tile) after the scores; mm3_index_decode asks for the scores
+    only.  Decode batches, topk above 16 and rows past 512 blocks cannot take
+    the fused call (MM3_EUNSUPPORTED, size 0)."""
+    lib = B.lib()
+    dec_ws = lambda p, k=16, so=0: lib.mm3_index_decode_workspace_bytes(ctypes.byref(p), k, so)
+    sel_ws = lambda p, k=16, so=0: lib.mm3_index_prefill_select_workspace_bytes(ctypes.byref(p), k, so)
+    r256 = lambda n: -(-n // 256) * 256
+    p = _problem(heads=4, num_reqs=4, query_len=8192, max_seq_len=16384, bt_width=128,
+                 bt_row_stride=128)
+    units = 4 * 64  # 4 requests x (4 * 8192 / 512) row tiles
+    assert dec_ws(p) == r256(4 * 32768 * 128 * 4)
+    assert sel_ws(p) == r256(4 * 32768 * 128 * 4) + r256(2 * units * 4)
+    assert sel_ws(p, so=1) == r256(2 * units * 4)
+    assert sel_ws(p, k=17) == 0 and "topk <= 16" in lib.mm3_last_error().decode()
+    wide = _problem(heads=4, num_reqs=4, query_len=8192, max_seq_len=65537, bt_width=513,
+                    bt_row_stride=513)
+    assert sel_ws(wide, so=1) == 0
+    dec = _problem(heads=4, num_reqs=8, query_len=4, max_seq_len=8192)
+    assert sel_ws(dec, so=1) == 0
+    out = ctypes.c_void_p(FAKE * 5)
+    rc = lib.mm3_index_prefill_select(ctypes.byref(dec), 16, 1, 2, out, 32 * 16, 16, None, 0, 0, 0,
+                                      ctypes.c_void_p(FAKE * 6), 1 << 20, None)
+    assert rc == B.MM3_EUNSUPPORTED
+    rc = lib.mm3_index_prefill_select(ctypes.byref(p), 16, 1, 2, out, 32768 * 16, 16, None, 0, 0, 0,
+                                      ctypes.c_void_p(FAKE * 6), 1 << 20, None)
+    assert rc == B.MM3_EWORKSPACE

@@ -1033,3 +1033,101 @@ def test_ballot_selector_many_rows(nb, topk):
     torch.cuda.synchronize()
     want = oracle.topk(s.cpu().numpy(), seq.cpu().numpy(), Q, topk, 1, 2)
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+# ------------------------------------------- fused prefill selection
+#
+# mm3_index_prefill_select: the prefill scorer with the selection inside it
+# (the workgroup completing a row tile selects its rows).  Its ids and scores
+# must equal the two-launch path's and the oracle's.
+
+def run_prefill_select(w, with_scores=False, ws_fill=0x5A):
+    scores = (torch.full((w.heads, w.rows, w.score_width), float("nan"), device=DEV)
+              if with_scores else None)
+    out = torch.full((w.heads, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
+    p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                         w.sm_scale, w.kscales)
+    n = mm3.prefill_select_workspace_bytes(p, w.topk, with_scores)
+    ws = torch.full((n,), ws_fill, dtype=torch.uint8, device=DEV)  # stale contents
+    mm3.mm3_index_prefill_select(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                 w.max_seq_len, w.sm_scale, w.topk, w.init_blocks, w.local_blocks,
+                                 kscales=w.kscales, out=out, scores_out=scores, workspace=ws)
+    torch.cuda.synchronize()
+    return scores, out
+
+
+FUSED_PREFILL = [
+    # (label, make kwargs); lanes per row in the fused selection by row width
+    ("nb64_h4", dict(R=2, lens=(5000, 8000), Q=700, H=4, max_seq_len=8192, topk=16, I=1, L=2)),
+    ("nb128_h4", dict(R=3, lens=(3000, 16000), Q=900, H=4, max_seq_len=16384, topk=16, I=1, L=2)),
+    ("nb256_h2", dict(R=2, lens=(9000, 32000), Q=1100, H=2, max_seq_len=32768, topk=12, I=2, L=3)),
+    ("nb512_h1", dict(R=2, lens=(20000, 65000), Q=1500, H=1, max_seq_len=65536, topk=16, I=1, L=2)),
+    ("seq_shorter_than_q", dict(R=4, lens=(0, 0), Q=600, H=1, max_seq_len=1024, topk=4, I=1, L=1,
+                                fixed_lens=[100, 700, 0, 1])),
+    ("many_tiles_mixed", dict(R=12, lens=(100, 5000), Q=700, H=4, max_seq_len=8192, topk=16, I=1, L=2)),
+    ("h8_tail_tile", dict(R=3, lens=(1000, 3000), Q=65, H=8, max_seq_len=4096, topk=8, I=1, L=1)),
+    ("heads_17_q1", dict(R=3, lens=(500, 4000), Q=1, H=17, max_seq_len=4096, topk=16, I=1, L=2)),
+    ("h3_split_positions", dict(R=3, lens=(2000, 6000), Q=400, H=3, max_seq_len=8192, topk=16, I=0,
+                                L=0)),
+]
+
+
+@pytest.mark.parametrize("kfmt", [KFMT_BF16, KFMT_NVFP4], ids=["bf16", "nvfp4"])
+@pytest.mark.parametrize("label,kw", FUSED_PREFILL, ids=[e[0] for e in FUSED_PREFILL])
+def test_fused_prefill_selection(label, kw, kfmt):
+    w = make(name=label, kfmt=kfmt, seed=len(label) + 31 * kfmt, device=DEV, **kw)
+    _say(f"fused prefill {label} kfmt={kfmt}: rows={w.rows} H={w.heads} nb={w.nb_max}")
+    s_f, out_f = run_prefill_select(w, with_scores=True)
+    full_check(w, s_f, out_f, f"fused prefill {label}")
+    _, out_ws = run_prefill_select(w, ws_fill=0xFF)
+    _, out_two = run_fused(w, with_scores=False)  # scorer, then selector
+    assert torch.equal(out_f, out_ws) and torch.equal(out_f, out_two)
+
+
+def test_full_size_fused_prefill_selection():
+    """The chunked prefill at full size through the fused call: ids equal
+    the scorer-then-selector path's (which the full-size test compares with
+    the oracle row by row), for bf16 and NVFP4 keys; the fused call also
+    writes the same scores."""
+    for kfmt in (KFMT_BF16, KFMT_NVFP4):
+        w = config(4, device=DEV, kfmt=kfmt)
+        s_two, out_two = run_split(w)
+        s_f, out_f = run_prefill_select(w, with_scores=True)
+        _, out_ws = run_prefill_select(w)
+        assert torch.equal(out_f, out_two) and torch.equal(out_ws, out_two)
+        assert torch.equal(torch.nan_to_num(s_f, nan=7.0), torch.nan_to_num(s_two, nan=7.0))
+
+
+def test_graph_capture_fused_prefill():
+    """The fused prefill selection captured once (its reset kernel and scorer);
+    replays after new lengths and queries are written in place match eager
+    calls, with eager work and synchronisation between replays."""
+    w = make(name="graph_fused", R=3, lens=(3000, 8000), Q=700, H=4, max_seq_len=8192, topk=16, I=1,
+             L=2, kfmt=KFMT_BF16, seed=57, device=DEV)
+    out = torch.full((w.heads, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
+    p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                         w.sm_scale)
+    ws = torch.empty(mm3.prefill_select_workspace_bytes(p, w.topk, False), dtype=torch.uint8,
+                     device=DEV)
+    call = lambda: mm3.mm3_index_prefill_select(w.q, w.kdata, w.block_table, w.seq_lens,
+                                                w.query_len, w.max_seq_len, w.sm_scale, w.topk,
+                                                w.init_blocks, w.local_blocks, out=out,
+                                                workspace=ws)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    for it in range(4):
+        w.seq_lens.copy_(torch.randint(700, 8193, (w.num_reqs,), generator=gen, device=DEV).to(torch.int32))
+        w.q.copy_(torch.randn(w.q.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        _, want = run_split(w)
+        assert torch.equal(got, want), f"replay {it} differs from the scorer-then-selector path"
+        invariants(w, got)
