@@ -153,6 +153,9 @@ typedef struct mm3_problem {
  * expected finite: a score whose block holds a NaN or infinite product is
  * unspecified.
  */
+/* (scores, and the problem's block_table, may be NULL when
+ * cdiv(max_seq_len, 128) == 0: no row sees a block, so nothing is read or
+ * written there; the same holds for the selection calls below.) */
 int mm3_index_score(const mm3_problem* p, float* scores, int64_t s_head_stride,
                     int64_t s_row_stride, int32_t s_width, void* stream);
 

@@ -366,8 +366,9 @@ def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm
 def prefill_select_workspace_bytes(p: Problem, topk: int, with_scores_out: bool) -> int:
     n = lib().mm3_index_prefill_select_workspace_bytes(ctypes.byref(p), int(topk),
                                                        int(with_scores_out))
-    if n == 0:
-        raise Mm3Error(MM3_EUNSUPPORTED, lib().mm3_last_error().decode())
+    err = lib().mm3_last_error().decode()
+    if n == 0 and err:
+        raise Mm3Error(MM3_EUNSUPPORTED, err)
     return n
 
 
@@ -383,8 +384,8 @@ def mm3_index_prefill_select(q, kdata, block_table, seq_lens, query_len, max_seq
     if out.dtype != torch.int32 or out.dim() != 3 or out.stride(2) != 1:
         raise ValueError("out must be int32 [heads, >=tokens, topk] with unit column stride")
     if workspace is None:
-        workspace = torch.empty(prefill_select_workspace_bytes(p, topk, scores_out is not None),
-                                dtype=torch.uint8, device=q.device)
+        n = prefill_select_workspace_bytes(p, topk, scores_out is not None)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
     if scores_out is not None:
         if scores_out.dtype != torch.float32 or scores_out.stride(2) != 1:
             raise ValueError("scores_out must be fp32 with unit column stride")

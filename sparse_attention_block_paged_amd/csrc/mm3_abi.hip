@@ -94,7 +94,7 @@ int check_problem(const mm3_problem* p) {
   if (p->kfmt != MM3_KFMT_BF16 && p->kfmt != MM3_KFMT_NVFP4)
     return fail(MM3_EINVAL, "unknown index-K format %d", p->kfmt);
   if (p->num_pages < 1) return fail(MM3_EINVAL, "index cache must hold >= 1 page");
-  if (!p->q || !p->kdata || !p->block_table)
+  if (!p->q || !p->kdata || (!p->block_table && nb > 0))
     return fail(MM3_EINVAL, "q, kdata and block_table must be non-NULL");
   if (p->kfmt == MM3_KFMT_NVFP4 && !p->kscales)
     return fail(MM3_EINVAL, "NVFP4 index cache needs kscales");
@@ -115,7 +115,7 @@ int check_problem(const mm3_problem* p) {
 int check_scores(const mm3_problem* p, const float* s, int64_t sh, int64_t sr, int32_t sw) {
   const int64_t T = p->rows.total_q;
   const int64_t nb = cdiv64(p->rows.max_seq_len, MM3_BLOCK);
-  if (!s) return fail(MM3_EINVAL, "scores must be non-NULL");
+  if (!s && nb > 0) return fail(MM3_EINVAL, "scores must be non-NULL");
   if (!aligned(s, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
   if (sw < nb) return fail(MM3_EINVAL, "score width %d < cdiv(max_seq_len,128) = %lld", sw, (long long)nb);
   if (T > 1 && sr < sw) return fail(MM3_EINVAL, "score row stride must be >= score width");
@@ -353,7 +353,7 @@ int mm3_index_topk(const float* scores, int64_t s_head_stride, int64_t s_row_str
   const int64_t nb = cdiv64(rows->max_seq_len, MM3_BLOCK);
   if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
   const int64_t T = rows->total_q;
-  if (!scores) return fail(MM3_EINVAL, "scores must be non-NULL");
+  if (!scores && nb > 0) return fail(MM3_EINVAL, "scores must be non-NULL");
   if (!aligned(scores, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
   if (s_width < nb) return fail(MM3_EINVAL, "score width < cdiv(max_seq_len,128)");
   if (s_head_stride < 0 || s_row_stride < 0) return fail(MM3_EINVAL, "score strides must be non-negative");
@@ -386,7 +386,7 @@ int mm3_index_topk_blocks(const float* scores, int64_t s_head_stride, int64_t s_
   if (!row_blocks) return fail(MM3_EINVAL, "row_blocks must be non-NULL");
   if (!aligned(row_blocks, 4)) return fail(MM3_EINVAL, "row_blocks must be 4-byte aligned");
   const int64_t T = total_q;
-  if (!scores) return fail(MM3_EINVAL, "scores must be non-NULL");
+  if (!scores && nb > 0) return fail(MM3_EINVAL, "scores must be non-NULL");
   if (!aligned(scores, 4)) return fail(MM3_EINVAL, "scores must be 4-byte aligned");
   if (s_width < nb) return fail(MM3_EINVAL, "score width < cdiv(max_seq_len,128)");
   if (s_head_stride < 0 || s_row_stride < 0) return fail(MM3_EINVAL, "score strides must be non-negative");
@@ -426,6 +426,8 @@ size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk, int3
 size_t mm3_index_prefill_select_workspace_bytes(const mm3_problem* p, int32_t topk, int32_t with_scores_out) {
   if (check_problem(p)) return 0;
   if (check_select(topk, 0, 0)) return 0;
+  if (p->rows.total_q == 0) return ok(), 0;  // nothing to score or select
+  if (p->rows.max_seq_len == 0) return ok(), workspace_score_bytes(p, with_scores_out);
   const int nctr = fused_prefill_counters(p, topk, nullptr);
   if (nctr == 0) {
     fail(MM3_EUNSUPPORTED, "the batch cannot take the fused prefill selection (it needs a uniform batch "
@@ -518,6 +520,11 @@ int mm3_index_prefill_select(const mm3_problem* p, int32_t topk, int32_t init_bl
   if ((rc = check_select(topk, init_blocks, local_blocks))) return rc;
   const int64_t T = p->rows.total_q;
   if ((rc = check_out(out, o_head_stride, o_row_stride, p->heads, T, topk))) return rc;
+  if (T == 0) return ok();
+  if (p->rows.max_seq_len == 0)  // no row sees a block: the selector writes the -1 rows
+    return mm3_index_decode(p, topk, init_blocks, local_blocks, out, o_head_stride, o_row_stride,
+                            scores_out, s_head_stride, s_row_stride, s_width, workspace,
+                            workspace_bytes, nullptr, stream);
   const int nctr = fused_prefill_counters(p, topk, nullptr);
   if (nctr == 0)
     return fail(MM3_EUNSUPPORTED, "the batch cannot take the fused prefill selection (it needs a uniform "

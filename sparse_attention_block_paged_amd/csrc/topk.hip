@@ -188,7 +188,27 @@ static TopkPlan plan_topk(const TopkArgs& a) {
   return p;
 }
 
+// No row of the batch sees a block (cdiv(max_seq_len, 128) == 0): every id
+// is -1, and with a sparse table every slot -1 and every context length 0.
+// The selectors are not launched then: their branch-free row loads assume a
+// score row of at least one column.
+__global__ __launch_bounds__(256) void no_blocks_kernel(TopkArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= a.rows.tokens) return;
+  for (int h = 0; h < a.heads; ++h)
+    for (int k = lane; k < a.topk; k += 64) a.out[(int64_t)h * a.o_head + (int64_t)t * a.o_row + k] = -1;
+  if (a.sparse) {
+    int32_t* st = a.sp.table + (int64_t)t * a.sp.st_row;
+    for (int x = lane; x < a.topk * a.sp.pages_per_block; x += 64) st[x] = -1;
+    if (lane == 0) a.sp.ctx_lens[t] = 0;
+  }
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.nb_max == 0) {
+    hipLaunchKernelGGL(no_blocks_kernel, dim3((a.rows.tokens + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const TopkPlan p = plan_topk(a);
   if (p.split) {
     if (p.rowb)
@@ -207,6 +227,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 const char* topk_kernel_name(const TopkArgs& a) {
+  if (a.nb_max == 0) return "no_blocks_kernel";
   const TopkPlan p = plan_topk(a);
   static thread_local char buf[96];
   if (p.split)

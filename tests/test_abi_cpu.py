@@ -357,6 +357,8 @@ def _selector(s_ptr=FAKE, sh=None, sr=128, sw=128, heads=4, T=32768, msl=16384, 
     (dict(heads=1, T=8, msl=200000, sw=1568, sr=1568), "topk_kernel<0, false, 1, false>"),
     # unaligned scores cannot take the lanes' 16-byte loads
     (dict(s_ptr=FAKE + 4), "topk_kernel<2, false, 4, false>"),
+    # no row sees a block: no selector reads scores
+    (dict(msl=0, sw=0, sr=0), "no_blocks_kernel"),
 ])
 def test_selector_query_names_the_launched_kernel(kw, want):
     assert _selector(**kw) == want
@@ -417,3 +419,15 @@ def test_fused_prefill_workspace_sizes():
     rc = lib.mm3_index_prefill_select(ctypes.byref(p), 16, 1, 2, out, 32768 * 16, 16, None, 0, 0, 0,
                                       ctypes.c_void_p(FAKE * 6), 1 << 20, None)
     assert rc == B.MM3_EWORKSPACE
+
+
+def test_fused_prefill_empty_batch_succeeds():
+    """No rows: nothing to score or select, no workspace needed, MM3_OK (as
+    every entry point does for an empty batch)."""
+    lib = B.lib()
+    p = _problem(heads=4, num_reqs=0, query_len=700, total_q=0, max_seq_len=8192)
+    assert lib.mm3_index_prefill_select_workspace_bytes(ctypes.byref(p), 16, 0) == 0
+    assert lib.mm3_last_error().decode() == ""
+    rc = lib.mm3_index_prefill_select(ctypes.byref(p), 16, 1, 2, ctypes.c_void_p(FAKE * 5), 0, 16,
+                                      None, 0, 0, 0, None, 0, None)
+    assert rc == B.MM3_OK

@@ -1084,6 +1084,32 @@ def test_fused_prefill_selection(label, kw, kfmt):
     assert torch.equal(out_f, out_ws) and torch.equal(out_f, out_two)
 
 
+def test_no_visible_blocks_anywhere():
+    """max_seq_len 0 (no row sees a block, score rows have no column): every
+    id -1 and every sparse slot -1 with context length 0, through each entry
+    point, and no selector reads the (empty) score rows."""
+    w = make(name="no_keys", R=2, lens=(0, 0), Q=40, H=1, max_seq_len=0, topk=4, I=1, L=1,
+             kfmt=KFMT_BF16, seed=3, device=DEV, fixed_lens=[0, 0])
+    assert mm3.mm3_index_topk_selector(torch.empty((1, w.rows, 0), device=DEV), w.rows, 0,
+                                       w.topk) == "no_blocks_kernel"
+    _, out = run_prefill_select(w)
+    assert torch.all(out == -1)
+    _, out = run_fused(w, with_scores=False)
+    assert torch.all(out == -1)
+    _, out = run_split(w)
+    assert torch.all(out == -1)
+    abt = torch.zeros((w.num_reqs, 1), dtype=torch.int32, device=DEV)
+    st = torch.full((w.rows, w.topk), 7, dtype=torch.int32, device=DEV)
+    ctx = torch.full((w.rows,), 7, dtype=torch.int32, device=DEV)
+    out = torch.full((1, w.rows, w.topk), 7, dtype=torch.int32, device=DEV)
+    mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                         w.sm_scale, w.topk, w.init_blocks, w.local_blocks, out=out,
+                         attention_block_table=abt, sparse_block_table_out=st,
+                         sparse_context_lens_out=ctx, pages_per_block=1, block_page_stride=1)
+    torch.cuda.synchronize()
+    assert torch.all(out == -1) and torch.all(st == -1) and torch.all(ctx == 0)
+
+
 def test_full_size_fused_prefill_selection():
     """The chunked prefill at full size through the fused call: ids equal
     the scorer-then-selector path's (which the full-size test compares with
