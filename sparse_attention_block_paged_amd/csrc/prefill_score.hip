@@ -311,19 +311,28 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
   constexpr int kCopyRound = 1024 * kPfWaves;
   const int t0 = 4 * wave + (lane >> 4);
   const uint32_t src0 = t0 * (kDim * 2) + (((lane & 15) ^ (t0 & 15)) << 4);
-  auto copy_page = [&](uint8_t* kl, const PfCursor& c) __attribute__((always_inline)) {
-    const uint8_t* pg = a.kdata + (int64_t)bt_s[(int64_t)c.r * a.bt_stride + c.b] * kPageBytes;
-    const uint32_t l0 = (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)kl + 1024 * wave;
-    // the round steps go on the scalar base: one offset register for all
-#pragma unroll
-    for (int k = 0; k < kPfCopies; ++k) copy16_to_lds(l0 + kCopyRound * k, pg + kCopyRound * k, src0);
+  // copy k of page pg into the buffer whose wave slot is l0 (the round steps
+  // go on the scalar base: one offset register for all)
+  auto copy_one = [&](uint32_t l0, const uint8_t* pg, int k) __attribute__((always_inline)) {
+    copy16_to_lds(l0 + kCopyRound * k, pg + kCopyRound * k, src0);
+  };
+  auto wave_slot = [&](uint8_t* kl) { return (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)kl + 1024 * wave; };
+  auto page_bytes = [&](int64_t page) -> const uint8_t* { return a.kdata + page * kPageBytes; };
+  // The page id of a step, by a vector load: issued a step before its copy,
+  // it completes behind that step's multiplies (the ring barrier waits for
+  // it), where a scalar load right before the copy would hold the wave for
+  // its latency at every step.  The opaque zero offset keeps it a vector
+  // load.
+  auto page_load = [&](const PfCursor& c) __attribute__((always_inline)) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return a.bt[(int64_t)c.r * a.bt_stride + c.b + z];
   };
 
   // NVFP4: copy k of wave w moves nibble KiB kPfWaves k + w of the page (the
   // 8 KiB in 8 / kPfWaves rounds), and wave 0 also moves the 1 KiB of scales,
   // into staging slot `slot`.
-  auto copy_fp4 = [&](int slot, const PfCursor& c) __attribute__((always_inline)) {
-    const int64_t page = bt_s[(int64_t)c.r * a.bt_stride + c.b];
+  auto copy_fp4 = [&](int slot, int64_t page) __attribute__((always_inline)) {
     const uint8_t* nib = a.kdata + page * kFp4NibBytes;
     const uint32_t l0 =
         (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Stage0 + slot * kFp4NibBytes) + 1024 * wave;
@@ -514,40 +523,77 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
   if constexpr (KFMT == 1) {
     if (threadIdx.x < 256) fill_lut(lut);  // read after the first ring barrier
   }
+  // the first page is on its way while the query rows load
+  {
+    const int64_t pg0 = bt_s[(int64_t)cur.r * a.bt_stride + cur.b];
+    if constexpr (KFMT == 0) {
+#pragma unroll
+      for (int k = 0; k < kPfCopies; ++k) copy_one(wave_slot(kbuf0), page_bytes(pg0), k);
+    } else {
+      copy_fp4(0, pg0);
+    }
+  }
+  // nn: the step two after the current one (page id in pg_next, loaded
+  // during the step before)
+  PfCursor nn = cur;
+  int pg_next = 0;
+  if (nsteps > 1) {
+    advance(nn);
+    pg_next = page_load(nn);
+  }
   load_q();
-  PfCursor nxt = cur;
-  if constexpr (KFMT == 0)
-    copy_page(kbuf0, nxt);
-  else
-    copy_fp4(0, nxt);
+  // Two workgroups share each CU, and at equal priority the SIMDs favour the
+  // older one's waves, so left alone the first-dispatched workgroup runs
+  // ahead and the other finishes its share alone, which keeps only half of
+  // the CU's waves busy (0.24 instead of 0.31 steps per us).  Priority
+  // falling with the progress through the share lets the one behind catch up
+  // at each band, so the two finish close together.  Step i is below b% of
+  // the share iff 100 i < b nsteps, i.e. i < ceil(b nsteps / 100).
+  auto band = [&](int b) { return (int)(((int64_t)b * nsteps + 99) / 100); };
+  const int band70 = band(70), band85 = band(85), band95 = band(95);
   int bfirst = cur.b, nst = 0, tile_done = 0;
+  // A full stage in the middle of a tile is written out after the next
+  // step's barrier, not before it: that barrier waits for all of the wave's
+  // vector memory operations, and stores issued just before it would hold
+  // every wave of the workgroup there for their completion.
+  bool flush_due = false;
   const int u_first = cur.u;
   for (int i = 0; i < nsteps; ++i) {
     uint8_t* const kl = (KFMT == 0 && (i & 1)) ? kbuf1 : kbuf0;
     ring_sync();
-    // Two workgroups share each CU, and at equal priority the SIMDs favour
-    // the older one's waves, so left alone the first-dispatched workgroup
-    // runs ahead and the other finishes its share alone, which keeps only
-    // half of the CU's waves busy (0.24 instead of 0.31 steps per us).
-    // Priority falling with the progress through the share lets the one
-    // behind catch up at each band, so the two finish close together.
     {
-      const int pct = (int)((int64_t)i * 100 / nsteps);
-      if (pct < 70)
+      if (i < band70)
         __builtin_amdgcn_s_setprio(3);
-      else if (pct < 85)
+      else if (i < band85)
         __builtin_amdgcn_s_setprio(2);
-      else if (pct < 95)
+      else if (i < band95)
         __builtin_amdgcn_s_setprio(1);
       else
         __builtin_amdgcn_s_setprio(0);
     }
     if (i + 1 < nsteps) {
-      advance(nxt);
-      if constexpr (KFMT == 0)
-        copy_page((i & 1) ? kbuf0 : kbuf1, nxt);
-      else
-        copy_fp4((i + 1) & 1, nxt);
+      // page of step i + 1 (its load has landed: the barrier waited for it)
+      asm volatile("" : "+v"(pg_next));
+      const int64_t pg = __builtin_amdgcn_readfirstlane(pg_next);
+      if (i + 2 < nsteps) {
+        advance(nn);
+        pg_next = page_load(nn);
+      }
+      if constexpr (KFMT == 0) {
+        const uint32_t l0 = wave_slot((i & 1) ? kbuf0 : kbuf1);
+#pragma unroll
+        for (int k = 0; k < kPfCopies; ++k) copy_one(l0, page_bytes(pg), k);
+      } else {
+        copy_fp4((i + 1) & 1, pg);
+      }
+    }
+    if (flush_due) {
+      // blocks bfirst .. bfirst + kPfStage - 1 of the current tile; cur is
+      // already at the next block of the same tile
+      flush(bfirst, kPfStage);
+      nst = 0;
+      bfirst = cur.b;
+      flush_due = false;
     }
     if constexpr (KFMT == 1) {
       // every wave is past step i - 1 (the ring barrier), so kbuf0 is free
@@ -559,10 +605,12 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
     const bool last = i + 1 == nsteps;
     const bool tile_end = cur.b + 1 == cur.nv;
     if constexpr (SEL == 0) {
-      if (nst == kPfStage || tile_end || last) {
+      if (tile_end || last) {
         flush(bfirst, nst);
         nst = 0;
         bfirst = cur.b + 1;
+      } else if (nst == kPfStage) {
+        flush_due = true;
       }
       if (!last) {
         advance(cur);
