@@ -93,6 +93,9 @@ constexpr int kPfLdsOf = KFMT == 0 ? kPfLds : kPfLdsFp4;
 // Above this many (request, row tile) units the start-finding scan of the
 // balanced grid costs more than it saves: one workgroup per unit instead.
 constexpr int kPfBalancedMaxUnits = 1 << 16;
+// Relative share sizes of workgroups on even- and odd-numbered XCDs.
+constexpr int kPfXcdWeightEven = 1030;
+constexpr int kPfXcdWeightOdd = 970;
 
 #define MM3_AS3 __attribute__((address_space(3)))
 #define MM3_AS4 __attribute__((address_space(4)))
@@ -233,11 +236,26 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
     total = __builtin_amdgcn_readfirstlane(total);
     // Workgroups are dealt to the 8 XCDs round-robin; renumber so that each
     // XCD takes one contiguous stretch of the list (its requests' pages stay
-    // in its own L2).
+    // in its own L2).  Under this load the odd-numbered XCDs run at a ~5%
+    // lower clock than the even ones (the same cycles per step, 1.70-1.74
+    // against 1.77-1.84 GHz), so their workgroups' shares are weighted
+    // 0.97 against 1.03.
     const int G = gridDim.x, g = blockIdx.x;
-    const int lg = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
-    const int64_t s0 = (int64_t)total * lg / G;
-    nsteps = (int)((int64_t)total * (lg + 1) / G - s0);
+    int64_t s0, s1;
+    if (G % 8 == 0) {
+      const int x = g % 8, per = G / 8;
+      const int64_t w_x = x % 2 == 0 ? kPfXcdWeightEven : kPfXcdWeightOdd;
+      // weight of the XCDs before x (half of them even), then of x's
+      // workgroups before this one
+      const int64_t w0 = (int64_t)per * ((x + 1) / 2 * kPfXcdWeightEven + x / 2 * kPfXcdWeightOdd) + w_x * (g / 8);
+      const int64_t wtot = (int64_t)per * 4 * (kPfXcdWeightEven + kPfXcdWeightOdd);
+      s0 = (int64_t)total * w0 / wtot;
+      s1 = (int64_t)total * (w0 + w_x) / wtot;
+    } else {
+      s0 = (int64_t)total * g / G;
+      s1 = (int64_t)total * (g + 1) / G;
+    }
+    nsteps = (int)(s1 - s0);
     if (part > 0 && pre <= s0 && s0 < pre + part) {
       int acc = pre;
       for (int v = lo; v < hi; ++v) {
