@@ -348,6 +348,23 @@ const char* mm3_index_topk_selector(const float* scores, int64_t s_head_stride,
                                     int32_t max_seq_len, int32_t topk,
                                     int32_t by_row_blocks, int32_t sparse);
 
+/*
+ * mm3_index_decode_launches -- how mm3_index_decode runs this problem: 1 when
+ * it scores and selects in one launch (every request holds at most 16 rows,
+ * heads * query_len <= 16, and sees at most 16 blocks, cdiv(max_seq_len, 128)
+ * <= 16; at most 256 requests; no sparse table; scores_out, if given,
+ * addressable through one buffer descriptor), 2 when it launches the scorer
+ * then the selector.  Both give identical scores and ids (page
+ * "ops.index_topk", minimax_m3_index_decode: score then select, one
+ * call); this names the path that runs, for tests and benchmarks.
+ * Arguments as in mm3_index_decode (scores_out is only inspected, with its
+ * strides).  Host only, no HIP call.  Returns 1 or 2, or a negative MM3_E*
+ * code with mm3_last_error() set when p is invalid.
+ */
+int mm3_index_decode_launches(const mm3_problem* p, const float* scores_out,
+                              int64_t s_head_stride, int64_t s_row_stride,
+                              const mm3_sparse_out* sparse);
+
 /* Message for the last non-OK return on this thread ("" if none).  Host
  * pointer, valid until the next call on this thread. */
 const char* mm3_last_error(void);

@@ -30,7 +30,7 @@ EXPORTED = (
     "mm3_index_score", "mm3_index_topk", "mm3_index_topk_blocks", "mm3_index_decode_workspace_bytes",
     "mm3_index_decode", "mm3_index_decode_static", "mm3_index_prefill_select",
     "mm3_index_prefill_select_workspace_bytes", "mm3_build_sparse_block_table",
-    "mm3_index_topk_selector", "mm3_last_error", "mm3_version",
+    "mm3_index_topk_selector", "mm3_index_decode_launches", "mm3_last_error", "mm3_version",
 )
 STATIC_SCRATCH_BYTES = 64 << 20
 
@@ -121,6 +121,8 @@ def lib():
         L.mm3_build_sparse_block_table.restype = ctypes.c_int
         L.mm3_index_topk_selector.argtypes = [P, I64, I64, I32, I32, I32, I32, I32, I32, I32]
         L.mm3_index_topk_selector.restype = ctypes.c_char_p
+        L.mm3_index_decode_launches.argtypes = [PP, P, I64, I64, PS]
+        L.mm3_index_decode_launches.restype = ctypes.c_int
         L.mm3_last_error.argtypes = []
         L.mm3_last_error.restype = ctypes.c_char_p
         L.mm3_version.argtypes = []
@@ -459,6 +461,22 @@ def mm3_build_sparse_block_table(topk_idx, seq_lens, query_len, max_seq_len,
         topk_idx.data_ptr(), topk_idx.stride(0), K, ctypes.byref(rows), ctypes.byref(sp),
         _stream(topk_idx, stream)))
     return sparse_table, sparse_ctx_lens
+
+
+def mm3_index_decode_launches(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale,
+                              kscales=None, scores_out=None, cu_seqlens_q=None, prefix_lens=None,
+                              sparse=None):
+    """How mm3_index_decode runs this problem: 1 (scores and selection in one
+    launch) or 2 (scorer, then selector).  sparse: a SparseOut or None."""
+    p = make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_scale, kscales,
+                     cu_seqlens_q, prefix_lens)
+    sh = sr = 0
+    if scores_out is not None:
+        sh, sr = scores_out.stride(0), scores_out.stride(1)
+    n = lib().mm3_index_decode_launches(ctypes.byref(p), _ptr(scores_out), sh, sr,
+                                        None if sparse is None else ctypes.byref(sparse))
+    _check(min(n, 0))
+    return n
 
 
 def mm3_index_topk_selector(scores, total_q, max_seq_len, topk, by_row_blocks=False,

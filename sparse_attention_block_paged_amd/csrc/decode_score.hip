@@ -33,6 +33,7 @@
 #include "mm3_fp4.h"
 #include "mm3_launch.h"
 #include "mm3_rows.h"
+#include "mm3_select.h"
 
 namespace mm3 {
 
@@ -330,14 +331,14 @@ __device__ __forceinline__ void score_wave(const ScoreArgs& a, const u32x2* lut,
   RingBlock<KFMT> ring[DB];
   if (!walk.first(ring[0].c)) return;
   QRows q;
-  {
-    const QRaw raw = issue_q<KFMT>(a, ring[0].c, n, g, true);
-    set_q<KFMT>(q, raw, a, ring[0].c, n);
-  }
+  // the first block's query rows and pages load together; the query operands
+  // are set up once both are on their way
+  const QRaw raw0 = issue_q<KFMT>(a, ring[0].c, n, g, true);
   ring[0].live = true;
   ring[0].new_req = false;
   issue_half<KFMT>(ring[0].h0, a, ring[0].c.page, 0, n, g, true);
   issue_half<KFMT>(ring[0].h1, a, ring[0].c.page, 1, n, g, true);
+  set_q<KFMT>(q, raw0, a, ring[0].c, n);
   Cur last = ring[0].c;  // the last block issued (the walker's position)
   bool more = true;      // the walker has not run out
 #pragma unroll
@@ -550,7 +551,8 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_score_cu(ScoreArgs
 // Grid (block chunks, requests): workgroup (x, r) covers blocks
 // [x*bpw, (x+1)*bpw) of request r and returns at once past its end.
 
-struct ChunkWalk {
+template <int STEP>
+struct ChunkWalkT {
   const ScoreArgs* a;
   int r;
   ReqRows rr;
@@ -565,13 +567,15 @@ struct ChunkWalk {
     return true;
   }
   __device__ __forceinline__ bool next(Cur& c) {
-    b += 4;
+    b += STEP;
     if (b >= b_end) return false;
     c.b = b;
     c.page = page_of(*a, r, b);
     return true;
   }
 };
+
+using ChunkWalk = ChunkWalkT<4>;
 
 template <int KFMT>
 __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
@@ -590,6 +594,69 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   ChunkWalk walk{&a, r, rr, b_begin + wave, min(nb, b_begin + a.blocks_per_wg)};
   score_wave<KFMT, false>(a, lut, tbuf[wave], walk, nullptr, nullptr);
+}
+
+// ---- small batches: scores and selection in one launch
+//
+// For requests that see few blocks the two-launch path is bound by latency:
+// two kernel launches and a score round trip through global memory for a
+// few microseconds of work.  Here one workgroup takes one request: its waves
+// score blocks wave, wave + W, ... with the same wave loop as the per-CU
+// scorer (so the scores are the same bits), the scores stay in the waves'
+// LDS stages (and go to global memory too when the caller asks for them),
+// and after a barrier each wave selects rows of the request from the LDS.
+// The selection is that of the selector kernels (page "ops.index_topk",
+// minimax_m3_index_topk; forced blocks pinned as in page
+// "indexer_cp_exchange", module docstring): block b of a row holds the
+// selection key key_of(score, b, nv, I, L), and the row takes the blocks of
+// rank < topk under (key descending, id ascending); with at most kSmallBlocks
+// blocks a lane per block counts its rank directly.
+
+template <int KFMT>
+__global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_small(ScoreArgs a, TopkArgs t) {
+  constexpr int W = kCuWaves<KFMT>;
+  __shared__ u32x2 lut[KFMT == 1 ? 256 : 1];
+  __shared__ float stage_v[W][kStage];
+  __shared__ int32_t stage_o[W][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[W][KFMT == 0 ? kTransposeBytes : 16];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // the table load goes out first, so its latency overlaps the row lookup's
+  u32x2 lut_v{0u, 0u};
+  if constexpr (KFMT == 1) {
+    if (threadIdx.x < 256) lut_v = lut_entry();
+  }
+  const ReqRows rr = req_rows<true>(a.rows, r);
+  if constexpr (KFMT == 1) {
+    if (threadIdx.x < 256) lut[threadIdx.x] = lut_v;
+    __syncthreads();
+  }
+  // at most kSmallBlocks when seq_lens <= max_seq_len, as every scorer
+  // assumes; clamped so that a length past it cannot index past the stage
+  const int nbr = min(req_blocks(rr.p0, rr.n), kSmallBlocks);
+  ChunkWalkT<W> walk{&a, r, rr, wave, nbr};
+  score_wave<KFMT, true>(a, lut, tbuf[wave], walk, stage_v[wave], stage_o[wave]);
+  __syncthreads();
+  const int H = a.heads;
+  const int HQ = H * a.rows.qlen;  // stage stride: column n holds row n = j H + h
+  for (int row = wave; row < H * rr.n; row += W) {
+    const int j = row / H, h = row - j * H;
+    const int nv = blocks_at(rr.p0 + j);
+    uint32_t key = 0;
+    if (lane < nbr) key = key_of(stage_v[lane % W][(lane / W) * HQ + row], lane, nv, t.init_blocks, t.local_blocks);
+    int rank = 0;
+#pragma unroll
+    for (int b = 0; b < kSmallBlocks; ++b) {
+      const uint32_t kb = (uint32_t)__builtin_amdgcn_readlane((int)key, b);
+      rank += (kb > key || (kb == key && b < lane)) ? 1 : 0;
+    }
+    const bool take = key != 0 && rank < t.topk;
+    const uint64_t m = __ballot(take);
+    int32_t* orow = t.out + (int64_t)h * t.o_head + (int64_t)(rr.row0 + j) * t.o_row;
+    if (take) orow[lanes_below(m)] = lane;
+    for (int k = __popcll(m) + lane; k < t.topk; k += 64) orow[k] = -1;
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -625,6 +692,14 @@ static hipError_t launch_decode(const ScoreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s) { return launch_decode<0>(a, s); }
+
+hipError_t launch_decode_small(const ScoreArgs& a, const TopkArgs& t, int kfmt, hipStream_t s) {
+  if (kfmt == 0)
+    hipLaunchKernelGGL(decode_small<0>, dim3(a.rows.num_reqs), dim3(64 * kCuWaves<0>), 0, s, a, t);
+  else
+    hipLaunchKernelGGL(decode_small<1>, dim3(a.rows.num_reqs), dim3(64 * kCuWaves<1>), 0, s, a, t);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s) { return launch_decode<1>(a, s); }
 

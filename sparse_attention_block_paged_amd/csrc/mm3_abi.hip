@@ -226,6 +226,19 @@ ScoreArgs score_args(const mm3_problem* p, float* s, int64_t sh, int64_t sr) {
 // Ragged batches may hold both kinds, so both launch, each taking only its
 // own requests (decided on the device from cu_seqlens_q); the decode one
 // sizes its query tile for the largest row count it can take.
+// Batches that mm3_index_decode scores and selects in one launch: every
+// request is a decode request (heads * query_len <= kDecodeRows) that sees at
+// most kSmallBlocks blocks, there are few enough of them for one workgroup
+// each, no sparse table is asked for, and scores_out (if given) is addressable
+// through one buffer descriptor.
+bool small_decode_ok(const mm3_problem* p, const float* scores_out, int64_t sh, int64_t sr,
+                     const mm3_sparse_out* sparse) {
+  const int64_t nb = cdiv64(p->rows.max_seq_len, MM3_BLOCK);
+  if (sparse || nb < 1 || nb > kSmallBlocks || p->rows.num_reqs > kSmallMaxReqs) return false;
+  if ((int64_t)p->heads * p->rows.query_len > kDecodeRows) return false;
+  return !scores_out || score_args(p, const_cast<float*>(scores_out), sh, sr).s_bytes > 0;
+}
+
 int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStream_t st) {
   ScoreArgs a = score_args(p, s, sh, sr);
   const bool bf16 = p->kfmt == MM3_KFMT_BF16;
@@ -469,6 +482,13 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   hipStream_t st = (hipStream_t)stream;
   TopkArgs a = topk_args(s, sh, sr, sw, p->heads, &p->rows, topk, init_blocks, local_blocks, out,
                          o_head_stride, o_row_stride);
+  if (small_decode_ok(p, scores_out, sh, sr, sparse)) {
+    // one launch: the scores stay on chip unless the caller asked for them
+    ScoreArgs sa = score_args(p, scores_out, sh, sr);
+    if (!scores_out) sa.s_bytes = 0;
+    const hipError_t e = launch_decode_small(sa, a, p->kfmt == MM3_KFMT_BF16 ? 0 : 1, st);
+    return e == hipSuccess ? ok() : hip_fail(e, "small-batch decode launch");
+  }
   if (sparse) {
     a.sp = sparse_of(sparse);
     a.sparse = 1;
@@ -477,6 +497,14 @@ int mm3_index_decode(const mm3_problem* p, int32_t topk, int32_t init_blocks,
   hipError_t e = launch_topk(a, st);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
+}
+
+int mm3_index_decode_launches(const mm3_problem* p, const float* scores_out, int64_t s_head_stride,
+                              int64_t s_row_stride, const mm3_sparse_out* sparse) {
+  const int rc = check_problem(p);
+  if (rc) return rc;
+  g_err.clear();
+  return small_decode_ok(p, scores_out, s_head_stride, s_row_stride, sparse) ? 1 : 2;
 }
 
 const char* mm3_index_topk_selector(const float* scores, int64_t s_head_stride, int64_t s_row_stride,

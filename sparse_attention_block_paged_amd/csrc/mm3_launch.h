@@ -92,6 +92,11 @@ struct SparseTableArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_decode_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_decode_score_nvfp4(const ScoreArgs& a, hipStream_t s);
+// Scores and selection in one launch, one workgroup per request, for
+// batches whose requests see at most kSmallBlocks blocks and hold at most
+// kDecodeRows rows each; no sparse table.  a.scores / a.s_bytes: where the
+// scores also go (s_bytes 0: nowhere).
+hipError_t launch_decode_small(const ScoreArgs& a, const TopkArgs& t, int kfmt, hipStream_t s);
 hipError_t launch_prefill_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_prefill_score_nvfp4(const ScoreArgs& a, hipStream_t s);
 // The prefill scorer with the selection fused in (every request of the batch
@@ -113,6 +118,10 @@ hipError_t launch_sparse_table(const SparseTableArgs& a, hipStream_t s);
 
 // Rows one decode-scorer MFMA tile holds (heads * query_len must fit).
 constexpr int kDecodeRows = 16;
+// Most blocks a request may see, and most requests, for the single-launch
+// small-batch path.
+constexpr int kSmallBlocks = 16;
+constexpr int kSmallMaxReqs = 256;
 // Flattened (token, head) rows of one prefill row tile.
 constexpr int kPrefillRows = 512;
 

@@ -364,6 +364,36 @@ def test_selector_query_names_the_launched_kernel(kw, want):
     assert _selector(**kw) == want
 
 
+def _launches(p, scores=None, sh=0, sr=0, sparse=None):
+    return B.lib().mm3_index_decode_launches(ctypes.byref(p), scores, sh, sr,
+                                             None if sparse is None else ctypes.byref(sparse))
+
+
+@pytest.mark.parametrize("kw,want", [
+    # 8 requests of 4 heads x 4 rows that see at most 16 blocks: one launch
+    (dict(max_seq_len=2048), 1),
+    (dict(max_seq_len=2049), 2),              # 17 blocks
+    (dict(max_seq_len=2048, num_reqs=256), 1),
+    (dict(max_seq_len=2048, num_reqs=257), 2),
+    (dict(max_seq_len=2048, heads=8), 2),     # 32 rows per request: the prefill scorer
+    (dict(max_seq_len=2048, heads=16, query_len=1, q_tok_stride=16 * 128), 1),
+    (dict(max_seq_len=0), 2),                 # no block: the selector alone writes the -1 rows
+])
+def test_decode_launches_query(kw, want):
+    assert _launches(_problem(**kw)) == want
+
+
+def test_decode_launches_query_scores_out_and_sparse():
+    p = _problem(max_seq_len=2048)
+    T = p.rows.total_q
+    assert _launches(p, FAKE * 5, T * 16, 16) == 1
+    # a score tensor past 2 GiB is not addressable through one buffer descriptor
+    assert _launches(p, FAKE * 5, 1 << 29, 16) == 2
+    assert _launches(p, sparse=B.SparseOut()) == 2
+    assert _launches(_problem(heads=0)) == B.MM3_EINVAL
+    assert "heads" in _err()
+
+
 def test_selector_query_rejects_invalid():
     assert _selector(topk=0) is None
     assert "topk" in B.lib().mm3_last_error().decode()

@@ -167,6 +167,64 @@ def test_tiny_decode_exact_ids():
     assert np.array_equal(out.cpu().numpy(), ids_ref)
 
 
+# ------------------------------------------------------------ one-launch small batches
+#
+# mm3_index_decode scores and selects batches of requests that see at most 16
+# blocks in one launch (one workgroup per request, scores kept on chip).
+
+ONE_LAUNCH = [
+    ("tiny_decode", dict(cid=1)),
+    ("decode_r16_h4", dict(cid=2, R=16, lens=(100, 2048), max_seq_len=2048)),
+    ("long_r256_h1_q1", dict(cid=3, R=256, lens=(1, 2048), Q=1, max_seq_len=2048)),
+    ("h16_q1", dict(cid=2, R=5, lens=(1, 1900), H=16, Q=1, max_seq_len=1900)),
+    ("h2_q8_rows_before_first_key", dict(cid=2, R=7, lens=(1, 600), H=2, Q=8, max_seq_len=640)),
+    ("topk_above_blocks", dict(cid=2, R=3, lens=(1000, 2000), topk=20, max_seq_len=2048)),
+    ("topk_all_forced", dict(cid=2, R=4, lens=(1500, 2048), topk=4, I=2, L=2, max_seq_len=2048)),
+    ("nvfp4", dict(cid=5, R=9, lens=(100, 2048), max_seq_len=2048)),
+    ("ragged_empty_requests", dict(cid=2, R=6, lens=(200, 2048), max_seq_len=2048, qlens=[(0, 4)] * 6)),
+    ("ragged_prefix_gap", dict(cid=2, R=5, lens=(300, 2048), max_seq_len=2048, qlens=[(1, 4)] * 5,
+                               prefix="gap")),
+]
+
+
+@pytest.mark.parametrize("label,kw", ONE_LAUNCH, ids=[e[0] for e in ONE_LAUNCH])
+def test_one_launch_small_batches(label, kw):
+    """Ids and scores against the oracle, and bit-equal to mm3_index_score
+    then mm3_index_topk (the two-launch kernels), with and without
+    scores_out."""
+    kw = dict(kw)
+    cid = kw.pop("cid")
+    w = small(cid, **kw)
+    probe = torch.empty((w.heads, w.rows, w.score_width), device=DEV)
+    assert mm3.mm3_index_decode_launches(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                         w.max_seq_len, w.sm_scale, kscales=w.kscales,
+                                         scores_out=probe, **_ragged_kw(w)) == 1
+    _say(f"case {label} (one launch)")
+    scores, out = run_fused(w, with_scores=True)
+    full_check(w, scores, out, label + " one launch")
+    s2, out2 = run_split(w)
+    assert torch.equal(out, out2), "one-launch ids differ from the two-launch kernels'"
+    assert torch.equal(scores.view(torch.int32), s2.view(torch.int32)), \
+        "one-launch scores differ from the two-launch scorer's (bits, or entries written)"
+    _, out3 = run_fused(w, with_scores=False)
+    assert torch.equal(out, out3)
+
+
+def test_one_launch_limits_take_two_launches():
+    """Just past the one-launch bounds (17 blocks; 257 requests) the call
+    takes the scorer and the selector, with the same oracle parity."""
+    for label, kw in (("17_blocks", dict(cid=2, R=4, lens=(2000, 2100), max_seq_len=2100)),
+                      ("257_requests", dict(cid=3, R=257, lens=(1, 1024), Q=1, max_seq_len=1024))):
+        kw = dict(kw)
+        cid = kw.pop("cid")
+        w = small(cid, **kw)
+        assert mm3.mm3_index_decode_launches(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                             w.max_seq_len, w.sm_scale, kscales=w.kscales) == 2
+        _say(f"case {label} (two launches)")
+        scores, out = run_fused(w, with_scores=True)
+        full_check(w, scores, out, label + " two launches")
+
+
 # ------------------------------------------------------------ forced ties
 #
 # Exact ties at the k-th boundary, pushed through the scorers: a block gets
