@@ -365,6 +365,10 @@ def measure(cid, torch, dev, steps, warmup, ncopies, graph=False, detail=True, k
                       ms=round(ms_topk, 4), achieved_gbs=round(sel_gbs, 1),
                       bytes=alg["selector_bytes"]),
         fused_prefill_select_ms=None if ms_fused is None else round(ms_fused, 4),
+        # decode steps: one launch (small batches) or scorer + selector
+        step_launches=None if prefill else mm3.mm3_index_decode_launches(
+            base.q, base.kdata, base.block_table, base.seq_lens, base.query_len, base.max_seq_len,
+            base.sm_scale, kscales=base.kscales, **rg(base)),
         scorer_ms_p10_p50_p90=pct_score,
         scorer_ms_each_launch_mean=round(ms_score_each, 4),
         scorer_ms_warm=None if ms_score_warm is None else round(ms_score_warm, 4),
@@ -406,6 +410,8 @@ def extra_line(res):
         e["step_frac_hbm"] = res["step_frac"]
     if res["fused_prefill_select_ms"] is not None:
         e["fused_prefill_select_ms"] = res["fused_prefill_select_ms"]
+    if res["step_launches"] is not None:
+        e["step_launches"] = res["step_launches"]
     if res["config_id"] == 1:
         e["us_per_step"] = round(res["ms_per_step"] * 1e3, 2)
         e["note"] = "latency only: 8 blocks of keys, too small for a roofline figure"
@@ -491,6 +497,7 @@ def main():
         "selector": res["selector"],
         "step_ms_graph": None if res["ms_graph"] is None else round(res["ms_graph"], 5),
         "fused_prefill_select_ms": res["fused_prefill_select_ms"],
+        "step_launches": res["step_launches"],
         "step_ms_p10_p50_p90": res["step_ms_p10_p50_p90"],
         "scorer_ms_p10_p50_p90": res["scorer_ms_p10_p50_p90"],
         "scorer_ms_each_launch_mean": res["scorer_ms_each_launch_mean"],
