@@ -596,6 +596,33 @@ __global__ __launch_bounds__(256) void decode_score_chunked(ScoreArgs a) {
   score_wave<KFMT, false>(a, lut, tbuf[wave], walk, nullptr, nullptr);
 }
 
+// Blocks b, b + STEP, ... below b_end of request r, the first one's page id
+// already loaded.
+template <int STEP>
+struct SmallWalk {
+  const ScoreArgs* a;
+  int r;
+  ReqRows rr;
+  int b, b_end;
+  int64_t page0;
+  __device__ __forceinline__ bool first(Cur& c) {
+    if (b >= b_end) return false;
+    c.r = r;
+    c.pk = pack_req(rr.p0, rr.n);
+    c.row0 = rr.row0;
+    c.b = b;
+    c.page = page0;
+    return true;
+  }
+  __device__ __forceinline__ bool next(Cur& c) {
+    b += STEP;
+    if (b >= b_end) return false;
+    c.b = b;
+    c.page = page_of(*a, r, b);
+    return true;
+  }
+};
+
 // ---- small batches: scores and selection in one launch
 //
 // For requests that see few blocks the two-launch path is bound by latency:
@@ -622,11 +649,14 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_small(ScoreArgs a,
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // the table load goes out first, so its latency overlaps the row lookup's
+  // the table load and the page id of the wave's first block (block
+  // `wave`, read only below cdiv(max_seq_len, 128), which the block table's
+  // width covers) go out first, so their latency overlaps the row lookup's
   u32x2 lut_v{0u, 0u};
   if constexpr (KFMT == 1) {
     if (threadIdx.x < 256) lut_v = lut_entry();
   }
+  const int64_t page0 = wave < a.nb_max ? page_of(a, r, wave) : 0;
   const ReqRows rr = req_rows<true>(a.rows, r);
   if constexpr (KFMT == 1) {
     if (threadIdx.x < 256) lut[threadIdx.x] = lut_v;
@@ -635,7 +665,7 @@ __global__ __launch_bounds__(64 * kCuWaves<KFMT>) void decode_small(ScoreArgs a,
   // at most kSmallBlocks when seq_lens <= max_seq_len, as every scorer
   // assumes; clamped so that a length past it cannot index past the stage
   const int nbr = min(req_blocks(rr.p0, rr.n), kSmallBlocks);
-  ChunkWalkT<W> walk{&a, r, rr, wave, nbr};
+  SmallWalk<W> walk{&a, r, rr, wave, nbr, page0};
   score_wave<KFMT, true>(a, lut, tbuf[wave], walk, stage_v[wave], stage_o[wave]);
   __syncthreads();
   const int H = a.heads;
