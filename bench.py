@@ -156,6 +156,7 @@ def burn_in(torch, dev, ms):
     b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     torch.cuda.synchronize()
     t_end = time.perf_counter() + ms / 1000.0
+    c = None
     while time.perf_counter() < t_end:
         for _ in range(8):
             c = a @ b
