@@ -148,8 +148,8 @@ typedef struct mm3_problem {
  *           dot product of q[t, h, :] and the key).
  * A request with heads * n_r <= 16 rows is scored by the bandwidth-bound
  * decode scorer, a larger one by the MFMA prefill scorer; a ragged batch may
- * mix both kinds in one call.  Both take either key format (the prefill
- * scorer decodes each NVFP4 page once into bf16 in LDS).  q and keys are
+ * mix both kinds in one call.  Both take either key format (both decode
+ * NVFP4 keys to bf16 in registers, just before the multiplies).  q and keys are
  * expected finite: a score whose block holds a NaN or infinite product is
  * unspecified.
  */

@@ -32,9 +32,14 @@
 //   * Each wave stages its rows' scores in LDS and writes them every 8 blocks
 //     as row-contiguous 32-byte runs (one 4-byte store per row and block would
 //     scatter over 64 rows per instruction).
-// Two workgroups (80 KiB of LDS each) share a CU, so one's barrier or copy
-// wait is covered by the other's multiplies; wave priorities that fall with
-// the progress through a share keep the two abreast to the end.
+//   * NVFP4 keys: the raw page (8 KiB of nibbles, 1 KiB of scales) is copied
+//     the same way, and each wave decodes the fragments it multiplies in
+//     registers, each k-step's 8 elements in the shadow of the previous
+//     k-step's multiplies (the same table decode as the decode scorer).
+// Two workgroups (80 KiB of LDS each with bf16 keys, 36 KiB with NVFP4) share
+// a CU, so one's barrier or copy wait is covered by the other's multiplies;
+// wave priorities that fall with the progress through a share keep the two
+// abreast to the end.
 //
 // Fused selection (SEL > 0; page "ops.index_topk": minimax_m3_index_score
 // followed by minimax_m3_index_topk, here in one launch).  A row tile's
@@ -79,15 +84,17 @@ constexpr int kPfCopies = kPageBytes / (kPfThreads * 16);    // 16-byte copies p
 constexpr int kPfStageFloats = kPfWaveRows * kPfStage;       // per wave
 constexpr int kPfLds = 2 * kPageBytes + kPfWaves * kPfStageFloats * 4;  // 80 KiB
 // NVFP4 keys: the page (8 KiB nibbles + 1 KiB scales) is copied into one of
-// two staging slots, then decoded once by the whole workgroup into a single
-// bf16 page buffer in the same swizzled layout.
+// two slots, and each wave decodes the fragments it multiplies in registers
+// (no decoded page in LDS).  Nibble row of token t (64 bytes, 4 chunks of 16):
+// chunk c at 16 (c ^ ((t >> 1) & 3)), so that a wave's 16-byte reads of one
+// chunk of 32 consecutive tokens hit distinct banks.
 constexpr int kFp4NibBytes = kBlock * kDim / 2;    // 8 KiB
 constexpr int kFp4ScaleBytes = kBlock * kDim / 16;  // 1 KiB
-constexpr int kPfFp4Stage0 = kPageBytes;                             // nibble slots
+constexpr int kPfFp4Stage0 = 0;                                      // nibble slots
 constexpr int kPfFp4Scale0 = kPfFp4Stage0 + 2 * kFp4NibBytes;       // scale slots
 constexpr int kPfFp4Lut = kPfFp4Scale0 + 2 * kFp4ScaleBytes;        // E4M3 table
 constexpr int kPfFp4Scores = kPfFp4Lut + 256 * 8;                   // score stage
-constexpr int kPfLdsFp4 = kPfFp4Scores + kPfWaves * kPfStageFloats * 4;  // 68 KiB
+constexpr int kPfLdsFp4 = kPfFp4Scores + kPfWaves * kPfStageFloats * 4;  // 36 KiB
 template <int KFMT>
 constexpr int kPfLdsOf = KFMT == 0 ? kPfLds : kPfLdsFp4;
 // Above this many (request, row tile) units the start-finding scan of the
@@ -99,10 +106,6 @@ constexpr int kPfXcdWeightOdd = 970;
 
 #define MM3_AS3 __attribute__((address_space(3)))
 #define MM3_AS4 __attribute__((address_space(4)))
-
-__device__ __forceinline__ int swz(int tok, int chunk) {
-  return tok * (kDim * 2) + ((chunk ^ (tok & 15)) << 4);
-}
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
@@ -144,15 +147,6 @@ __device__ __forceinline__ void ring_sync() {
   asm volatile("" ::: "memory");
 }
 
-// Workgroup barrier after LDS writes only: copies still in flight are not
-// waited for.
-__device__ __forceinline__ void lds_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Position in the list of (unit, block) steps: unit u = row tile x of
 // request r (rows row0.., n of them, positions p0..), its step count nv and
 // the current block b.
@@ -164,8 +158,8 @@ template <int KFMT, bool BALANCED, int SEL>
 __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(ScoreArgs a, int units, int tiles,
                                                                               TopkArgs sel, int32_t* ctr) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPfLdsOf<KFMT>];
-  // bf16: two page buffers.  NVFP4: one decoded page buffer plus two staging
-  // slots for the raw page.
+  // bf16: two page buffers (kbuf0, kbuf1).  NVFP4: two slots of raw nibbles
+  // and scales, and the E4M3 table.
   uint8_t* const kbuf0 = smem;
   uint8_t* const kbuf1 = smem + kPageBytes;
   float* const stage_all = reinterpret_cast<float*>(smem + (KFMT == 0 ? 2 * kPageBytes : kPfFp4Scores));
@@ -298,7 +292,10 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
       const uint16_t* qp = a.q + (int64_t)(cur.row0 + j) * a.q_tok + (int64_t)h * a.q_head;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4 v = ld16(qp + 16 * kk + 8 * kg);
+        // k-step kk: bf16 keys, dims 16kk + 8kg .. +8 (the swizzled page's
+        // chunk 2kk + kg); NVFP4 keys, dims 64kg + 8kk .. +8 (each lane half
+        // decodes one half of the token's nibble row)
+        const u32x4 v = ld16(qp + (KFMT == 0 ? 16 * kk + 8 * kg : 64 * kg + 8 * kk));
         if constexpr (KFMT == 0) {
           qb[qt][kk] = as_bf16x8(v);
         } else {
@@ -349,103 +346,145 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
 
   // NVFP4: copy k of wave w moves nibble KiB kPfWaves k + w of the page (the
   // 8 KiB in 8 / kPfWaves rounds), and wave 0 also moves the 1 KiB of scales,
-  // into staging slot `slot`.
+  // into slot `slot`.  Lane l fills the 16-byte slot p = l % 4 of token
+  // (base + l / 4), whose (t >> 1) & 3 is (l >> 3) & 3 (the base is a
+  // multiple of 16 tokens): it holds chunk p ^ ((l >> 3) & 3).
+  const uint32_t nsrc0 = 16 * (lane & ~3) + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
   auto copy_fp4 = [&](int slot, int64_t page) __attribute__((always_inline)) {
     const uint8_t* nib = a.kdata + page * kFp4NibBytes;
     const uint32_t l0 =
         (uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Stage0 + slot * kFp4NibBytes) + 1024 * wave;
 #pragma unroll
     for (int k = 0; k < kFp4NibBytes / kCopyRound; ++k)
-      copy16_to_lds(l0 + kCopyRound * k, nib + kCopyRound * k + 1024 * wave, 16 * lane);
+      copy16_to_lds(l0 + kCopyRound * k, nib + kCopyRound * k + 1024 * wave, nsrc0);
     if (wave == 0)
       copy16_to_lds((uint32_t)(uintptr_t)(MM3_AS3 uint8_t*)(smem + kPfFp4Scale0 + slot * kFp4ScaleBytes),
                     a.kscales + page * kFp4ScaleBytes, 16 * lane);
   };
-  // decode staging slot `slot` into kbuf0: thread t handles the 16-byte
-  // chunks q = t + kPfThreads j (token q/16, chunk q%16 = dims 8(q%16)..+8)
-  auto decode_fp4 = [&](int slot) __attribute__((always_inline)) {
-    const uint8_t* nib = smem + kPfFp4Stage0 + slot * kFp4NibBytes;
-    const uint8_t* scl = smem + kPfFp4Scale0 + slot * kFp4ScaleBytes;
-    // two chunks at a time: all eight in flight would need registers that
-    // the query operands and accumulators hold
-#pragma unroll 2
-    for (int j = 0; j < kBlock * 16 / kPfThreads; ++j) {
-      const int qc = threadIdx.x + kPfThreads * j;
-      const int tok = qc >> 4, c = qc & 15;
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(nib + tok * (kDim / 2) + 4 * c);
-      const u32x2 tab = lut[scl[tok * (kDim / 16) + (c >> 1)]];
-      *reinterpret_cast<u32x4*>(kbuf0 + swz(tok, c)) = fp4x8_to_bf16(x, tab);
-    }
-  };
-
   float* const stage = stage_all + wave * kPfStageFloats;
   // stage layout: row rho (0..127 of the wave), column c at rho*8 + (c ^ (rho & 7))
-  auto compute = [&](const uint8_t* kl, int b, int col) __attribute__((always_inline)) {
+  // Scores block b (its keys in page buffer kl, or NVFP4 slot `slot`) into
+  // stage column col.
+  auto compute = [&](const uint8_t* kl, int slot, int b, int col) __attribute__((always_inline)) {
     if (!(wave_live && wave_pos_max >= kBlock * b)) return;
     // every row of the wave sees the whole block
     const bool full = kBlock * b + (kBlock - 1) <= wave_pos_min;
     float m[kPfQt];
 #pragma unroll
     for (int qt = 0; qt < kPfQt; ++qt) m[qt] = -INFINITY;
-    // Key fragment of step st: tokens 32(st/8) + nl, 16-byte chunk
-    // 2(st%8) + kg, at swz().  With tok & 15 == nl & 15 == 2p + e, the chunk
-    // slot (2kk + kg) ^ (2p + e) is 2(kk ^ p) + (kg ^ e), so the address is
-    // a0 ^ (kk << 5) plus 8 KiB per token tile, a0 holding the kk = 0 slot
-    // (the buffers are 256-byte aligned, so bits 5..7 of a0 are exactly p).
-    // The asm hides a0's loop invariance: hoisted out of the step loop, the
-    // eight per-kk addresses would stay live next to the 192 query and
-    // accumulator registers and spill.
-    uint32_t a0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)kl + nl * (kDim * 2) +
-                  (((kg ^ nl) & 1) << 4) + (((nl >> 1) & 7) << 5);
-    asm volatile("" : "+v"(a0));
-    auto frag = [&](int st) {
-      const uint32_t addr = (a0 ^ ((st & 7) << 5)) + (st >> 3) * 32 * (kDim * 2);
-      return as_bf16x8(*(const MM3_AS3 u32x4*)(uintptr_t)addr);
-    };
-    // Fragments are read kPfAhead steps before their multiplies; the
-    // scheduling barrier at the end of each step pins that order (left
-    // alone, the scheduler sinks each read next to its use and the wave then
-    // waits out the full LDS latency at every step).
-    // Fragments are read kPfAhead steps before their multiplies; the
-    // scheduling barrier at the end of each step pins that order (left
-    // alone, the scheduler sinks each read next to its use and the wave then
-    // waits out the full LDS latency at every step).
-    bf16x8 fr[kPfAhead + 1];
-#pragma unroll
-    for (int p = 0; p < kPfAhead; ++p) fr[p] = frag(p);
     f32x16 acc[kPfQt];
+    // After token tile tt's last k-step: acc[qt][i] holds token
+    // 32tt + 8(i/4) + 4kg + i%4 against row nl of tile qt.
+    auto tile_max = [&](int tt) __attribute__((always_inline)) {
+      if (full) {
 #pragma unroll
-    for (int st = 0; st < 32; ++st) {
-      const int tt = st >> 3, kk = st & 7;
-      if (st + kPfAhead < 32) fr[(st + kPfAhead) % (kPfAhead + 1)] = frag(st + kPfAhead);
+        for (int qt = 0; qt < kPfQt; ++qt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m[qt] = fmaxf(m[qt], acc[qt][i]);
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < kPfQt; ++qt) {
+          // visible iff 8(i/4) + i%4 <= pos - 128b - 32tt - 4kg
+          const int d = pos_q[qt] - kBlock * b - 32 * tt - 4 * kg;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            m[qt] = fmaxf(m[qt], 8 * (i >> 2) + (i & 3) <= d ? acc[qt][i] : -INFINITY);
+        }
+      }
+    };
+    auto multiply = [&](const bf16x8& key, int kk) __attribute__((always_inline)) {
 #pragma unroll
       for (int qt = 0; qt < kPfQt; ++qt) {
         if (kk == 0) acc[qt] = f32x16{};
-        acc[qt] = mfma32(fr[st % (kPfAhead + 1)], qb[qt][kk], acc[qt]);
+        acc[qt] = mfma32(key, qb[qt][kk], acc[qt]);
       }
-      if (kk == 7) {
-        // acc[qt][i]: token 32tt + 8(i/4) + 4kg + i%4 against row nl of tile qt
-        if (full) {
+    };
+    if constexpr (KFMT == 0) {
+      // Key fragment of step st: tokens 32(st/8) + nl, 16-byte chunk
+      // 2(st%8) + kg, stored at slot chunk ^ (tok & 15) of the token's 256-byte
+      // row.  With tok & 15 == nl & 15 == 2p + e, the chunk
+      // slot (2kk + kg) ^ (2p + e) is 2(kk ^ p) + (kg ^ e), so the address is
+      // a0 ^ (kk << 5) plus 8 KiB per token tile, a0 holding the kk = 0 slot
+      // (the buffers are 256-byte aligned, so bits 5..7 of a0 are exactly p).
+      // The asm hides a0's loop invariance: hoisted out of the step loop, the
+      // eight per-kk addresses would stay live next to the 192 query and
+      // accumulator registers and spill.
+      uint32_t a0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)kl + nl * (kDim * 2) +
+                    (((kg ^ nl) & 1) << 4) + (((nl >> 1) & 7) << 5);
+      asm volatile("" : "+v"(a0));
+      auto frag = [&](int st) {
+        const uint32_t addr = (a0 ^ ((st & 7) << 5)) + (st >> 3) * 32 * (kDim * 2);
+        return as_bf16x8(*(const MM3_AS3 u32x4*)(uintptr_t)addr);
+      };
+      // Fragments are read kPfAhead steps before their multiplies; the
+      // scheduling barrier at the end of each step pins that order (left
+      // alone, the scheduler sinks each read next to its use and the wave then
+      // waits out the full LDS latency at every step).
+      bf16x8 fr[kPfAhead + 1];
 #pragma unroll
-          for (int qt = 0; qt < kPfQt; ++qt)
+      for (int p = 0; p < kPfAhead; ++p) fr[p] = frag(p);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m[qt] = fmaxf(m[qt], acc[qt][i]);
-        } else {
+      for (int st = 0; st < 32; ++st) {
+        const int tt = st >> 3, kk = st & 7;
+        if (st + kPfAhead < 32) fr[(st + kPfAhead) % (kPfAhead + 1)] = frag(st + kPfAhead);
+        multiply(fr[st % (kPfAhead + 1)], kk);
+        if (kk == 7) tile_max(tt);
+        // also keeps the next tile's multiplies (fresh accumulators) below the
+        // max: overlapping them needs a second set of 64 accumulator
+        // registers, which the two-waves-per-SIMD budget does not have (the
+        // other wave on the SIMD fills the matrix pipe meanwhile)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // NVFP4: lane (nl, kg) multiplies token 32tt + nl, dims 64kg + 8kk ..
+      // +8 at k-step (tt, kk): nibble dword kk of the lane's half row
+      // (chunks 2kg and 2kg + 1, words W0 for kk < 4 and W1 after), under
+      // scale byte kk / 2 of the token's scale word S (bytes 4kg .. 4kg + 3
+      // of its 8).  Each pair of k-steps takes one table entry L: the 8 E4M3
+      // codes of that scale, read two steps ahead.  W1 is read at kk = 0,
+      // the next tile's W0 at kk = 4, its S at kk = 0 and its first entry at
+      // kk = 6, so every read leads its use by two to six k-steps.
+      const int sw = (nl >> 1) & 3;
+      const uint32_t nb0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)(smem + kPfFp4Stage0 + slot * kFp4NibBytes);
+      const uint32_t sb0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)(smem + kPfFp4Scale0 + slot * kFp4ScaleBytes);
+      const uint32_t lb0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)(smem + kPfFp4Lut);
+      uint32_t w0a = nb0 + nl * (kDim / 2) + 16 * ((2 * kg) ^ sw);
+      uint32_t w1a = nb0 + nl * (kDim / 2) + 16 * ((2 * kg + 1) ^ sw);
+      uint32_t sa = sb0 + nl * (kDim / 16) + 4 * kg;
+      asm volatile("" : "+v"(w0a), "+v"(w1a), "+v"(sa));
+      auto ldw = [&](uint32_t base, int tt) {
+        return *(const MM3_AS3 u32x4*)(uintptr_t)(base + tt * 32 * (kDim / 2));
+      };
+      auto lds = [&](int tt) { return *(const MM3_AS3 uint32_t*)(uintptr_t)(sa + tt * 32 * (kDim / 16)); };
+      auto ldl = [&](uint32_t sword, int p) {
+        return *(const MM3_AS3 u32x2*)(uintptr_t)(lb0 + 8 * ((sword >> (8 * p)) & 0xFFu));
+      };
+      u32x4 W0 = ldw(w0a, 0), W1{};
+      uint32_t S = lds(0), Sn = 0;
+      u32x2 L[2];
+      L[0] = ldl(S, 0);
+      L[1] = u32x2{0u, 0u};
 #pragma unroll
-          for (int qt = 0; qt < kPfQt; ++qt) {
-            // visible iff 8(i/4) + i%4 <= pos - 128b - 32tt - 4kg
-            const int d = pos_q[qt] - kBlock * b - 32 * tt - 4 * kg;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              m[qt] = fmaxf(m[qt], 8 * (i >> 2) + (i & 3) <= d ? acc[qt][i] : -INFINITY);
+      for (int st = 0; st < 32; ++st) {
+        const int tt = st >> 3, kk = st & 7;
+        if (kk == 0) {
+          W1 = ldw(w1a, tt);
+          if (tt + 1 < 4) Sn = lds(tt + 1);
+        }
+        if (kk == 4 && tt + 1 < 4) W0 = ldw(w0a, tt + 1);
+        if ((kk & 1) == 0) {
+          if (kk < 6) {
+            L[((kk >> 1) + 1) & 1] = ldl(S, (kk >> 1) + 1);
+          } else if (tt + 1 < 4) {
+            S = Sn;
+            L[0] = ldl(S, 0);
           }
         }
+        const uint32_t x = kk < 4 ? W0[kk & 3] : W1[kk & 3];
+        multiply(as_bf16x8(fp4x8_to_bf16(x, L[(kk >> 1) & 1])), kk);
+        if (kk == 7) tile_max(tt);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // also keeps the next tile's multiplies (fresh accumulators) below the
-      // max: overlapping them needs a second set of 64 accumulator
-      // registers, which the two-waves-per-SIMD budget does not have (the
-      // other wave on the SIMD fills the matrix pipe meanwhile)
-      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int qt = 0; qt < kPfQt; ++qt) m[qt] = wave_max_xor32(m[qt]);
@@ -613,12 +652,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
       bfirst = cur.b;
       flush_due = false;
     }
-    if constexpr (KFMT == 1) {
-      // every wave is past step i - 1 (the ring barrier), so kbuf0 is free
-      decode_fp4(i & 1);
-      lds_sync();
-    }
-    compute(kl, cur.b, nst);
+    compute(kl, i & 1, cur.b, nst);
     ++nst;
     const bool last = i + 1 == nsteps;
     const bool tile_end = cur.b + 1 == cur.nv;
