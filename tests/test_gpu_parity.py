@@ -569,6 +569,42 @@ def test_graph_capture_replay_with_new_lengths():
         assert torch.equal(got, want), f"replay {it} differs from eager"
 
 
+def test_graph_capture_one_launch_small_batch():
+    """The one-launch small-batch path captured once; replays after new
+    device lengths and queries match eager calls and the two-launch
+    kernels."""
+    w = config(2, device=DEV, R=12, lens=(100, 2048), max_seq_len=2048)
+    assert mm3.mm3_index_decode_launches(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                         w.max_seq_len, w.sm_scale) == 1
+    out = torch.full((w.heads, w.rows, w.topk), -7, dtype=torch.int32, device=DEV)
+    p = mm3.make_problem(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len, w.max_seq_len,
+                         w.sm_scale)
+    ws = torch.empty(max(256, mm3.decode_workspace_bytes(p, w.topk, False)), dtype=torch.uint8,
+                     device=DEV)
+    call = lambda: mm3.mm3_index_decode(w.q, w.kdata, w.block_table, w.seq_lens, w.query_len,
+                                        w.max_seq_len, w.sm_scale, w.topk, w.init_blocks,
+                                        w.local_blocks, out=out, workspace=ws)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    for it in range(4):
+        new_lens = torch.randint(1, 2049, (w.num_reqs,), generator=gen, device=DEV).to(torch.int32)
+        w.seq_lens.copy_(new_lens)
+        w.q.copy_(torch.randn(w.q.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        _, want = run_fused(w, with_scores=False)
+        _, split = run_split(w)
+        assert torch.equal(got, want), f"replay {it} differs from eager"
+        assert torch.equal(got, split), f"replay {it} differs from the two-launch kernels"
+
+
 FULL = [1, 2, 3, 5]
 
 
