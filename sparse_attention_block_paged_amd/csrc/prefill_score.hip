@@ -75,6 +75,7 @@ constexpr int kPfQt = kPfWaveRows / 32;                      // 32-row MFMA B ti
 constexpr int kPfWgPerCu = 8 / kPfWaves;                     // two waves per SIMD
 static_assert(kPfWaves == 4 || kPfWaves == 8, "row tile");
 constexpr int kPfStage = 8;                                  // blocks staged per write-out
+static_assert(kPfStage == 8, "the write-out's lanes take two column groups of four");
 #ifndef MM3_PF_AHEAD
 #define MM3_PF_AHEAD 3
 #endif
@@ -362,7 +363,9 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
                     a.kscales + page * kFp4ScaleBytes, 16 * lane);
   };
   float* const stage = stage_all + wave * kPfStageFloats;
-  // stage layout: row rho (0..127 of the wave), column c at rho*8 + (c ^ (rho & 7))
+  // stage layout: row rho (0..127 of the wave), column c (block b & 7) at
+  // 8 rho + 4 ((c >> 2) ^ (rho & 1)) + (c & 3): a row's column groups of four
+  // stay contiguous for the write-out's 16-byte reads
   // Scores block b (its keys in page buffer kl, or NVFP4 slot `slot`) into
   // stage column col.
   auto compute = [&](const uint8_t* kl, int slot, int b, int col) __attribute__((always_inline)) {
@@ -493,37 +496,55 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
 #pragma unroll
     for (int u = 0; u < kPfQt / 2; ++u) {
       const int qt = (kPfQt / 2) * kg + u, r = 32 * qt + nl;
-      stage[r * kPfStage + (col ^ (r & 7))] = (kg ? m[kPfQt / 2 + u] : m[u]) * a.sm_scale;
+      stage[r * kPfStage + ((((col >> 2) ^ (r & 1)) << 2) | (col & 3))] =
+          (kg ? m[kPfQt / 2 + u] : m[u]) * a.sm_scale;
     }
   };
 
-  // write staged columns [0, nst) = blocks bfirst.. of the wave's rows; only
-  // visible (row, block) entries are written.  Lane l takes column l % 8 of
-  // rows l / 8 + 8k, k = 0..15.  Eight rows further on, a row's position,
-  // head and score offset move by fixed amounts (one carry when the head
-  // wraps), so the loop needs no division and no 64-bit multiply.
+  // Write the staged blocks bfirst .. bfirst + nst - 1 of the wave's rows (all
+  // in one group of eight, 8k .. 8k + 7; block b sits in stage column b & 7);
+  // only visible (row, block) entries are written.  Lane l takes column group
+  // g = l % 2 (columns 4g .. 4g + 3) of rows l / 2 + 32k, k = 0..3: a whole
+  // group goes out as one 16-byte store when its four blocks are staged and
+  // visible and the score layout is 16-byte aligned, else entry by entry.
+  // Thirty-two rows further on, a row's position, head and score offset move
+  // by fixed amounts (one carry when the head wraps), so the loop needs no
+  // division and no 64-bit multiply.
+  const bool vec_ok = (a.s_row & 3) == 0 && (a.s_head & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
   auto flush = [&](int bfirst, int nst) __attribute__((always_inline)) {
-    const int c = lane & 7, rl = lane >> 3;
-    const int b = bfirst + c;
+    const int g = lane & 1, rr = lane >> 1;
+    const int bb = (bfirst & ~7) + 4 * g;  // block of the group's column 0
+    const int q0 = max((bfirst & 7) - 4 * g, 0), q1s = min((bfirst & 7) + nst - 4 * g, 4);
     const int HQ = H * cur.n;
-    const int i0 = cur.x * kPrefillRows + kPfWaveRows * wave + rl;
-    int j = i0 / H, h = i0 - j * H;         // row i0: position p0 + j, head h
-    const int dj = 8 / H, dh = 8 - dj * H;  // the step of 8 rows
-    int64_t off = (int64_t)h * a.s_head + (int64_t)(cur.row0 + j) * a.s_row + b;
+    const int i0 = cur.x * kPrefillRows + kPfWaveRows * wave + rr;
+    int j = i0 / H, h = i0 - j * H;           // row i0: position p0 + j, head h
+    const int dj = 32 / H, dh = 32 - dj * H;  // the step of 32 rows
+    int64_t off = (int64_t)h * a.s_head + (int64_t)(cur.row0 + j) * a.s_row + bb;
     const int64_t doff = (int64_t)dh * a.s_head + (int64_t)dj * a.s_row;
     const int64_t wrap = a.s_row - (int64_t)H * a.s_head;
-    const float* sv = stage + rl * kPfStage + (c ^ rl);  // row rl + 8k at + 64k
-    const bool col_ok = c < nst;
+    // row rr + 32k: its group g at 8 (rr + 32k) + 4 (g ^ (rr & 1))
+    const float* sv = stage + rr * kPfStage + ((g ^ (rr & 1)) << 2);
     // all reads first: left next to their stores, each would wait out the
     // LDS latency inside its own branch
-    float v[kPfWaveRows / 8];
+    f32x4 v[kPfWaveRows / 32];
 #pragma unroll
-    for (int k = 0; k < kPfWaveRows / 8; ++k) v[k] = sv[8 * kPfStage * k];
+    for (int k = 0; k < kPfWaveRows / 32; ++k) v[k] = *reinterpret_cast<const f32x4*>(sv + 32 * kPfStage * k);
 #pragma unroll
-    for (int k = 0; k < kPfWaveRows / 8; ++k) asm volatile("" : "+v"(v[k]));
+    for (int k = 0; k < kPfWaveRows / 32; ++k) asm volatile("" : "+v"(v[k]));
 #pragma unroll
-    for (int k = 0; k < kPfWaveRows / 8; ++k) {
-      if (col_ok && i0 + 8 * k < HQ && cur.p0 + j >= kBlock * b) a.scores[off] = v[k];
+    for (int k = 0; k < kPfWaveRows / 32; ++k) {
+      if (i0 + 32 * k < HQ) {
+        const int pos = cur.p0 + j;
+        // columns q with block bb + q <= pos / 128 are visible
+        const int q1 = min(q1s, pos < 0 ? 0 : (pos >> 7) + 1 - bb);
+        if (vec_ok && q0 == 0 && q1 == 4) {
+          *reinterpret_cast<f32x4*>(a.scores + off) = v[k];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q >= q0 && q < q1) a.scores[off + q] = v[k][q];
+        }
+      }
       j += dj;
       h += dh;
       off += doff;
@@ -609,8 +630,8 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
   auto band = [&](int b) { return (int)(((int64_t)b * nsteps + 99) / 100); };
   const int band70 = band(70), band85 = band(85), band95 = band(95);
   int bfirst = cur.b, nst = 0, tile_done = 0;
-  // A full stage in the middle of a tile is written out after the next
-  // step's barrier, not before it: that barrier waits for all of the wave's
+  // A stage group completed (block 8k + 7) in the middle of a tile is written
+  // out after the next step's barrier, not before it: that barrier waits for all of the wave's
   // vector memory operations, and stores issued just before it would hold
   // every wave of the workgroup there for their completion.
   bool flush_due = false;
@@ -645,14 +666,14 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
       }
     }
     if (flush_due) {
-      // blocks bfirst .. bfirst + kPfStage - 1 of the current tile; cur is
-      // already at the next block of the same tile
-      flush(bfirst, kPfStage);
+      // blocks bfirst .. bfirst + nst - 1 of the current tile, up to a block
+      // 8k + 7; cur is already at the next block of the same tile
+      flush(bfirst, nst);
       nst = 0;
       bfirst = cur.b;
       flush_due = false;
     }
-    compute(kl, i & 1, cur.b, nst);
+    compute(kl, i & 1, cur.b, cur.b & (kPfStage - 1));
     ++nst;
     const bool last = i + 1 == nsteps;
     const bool tile_end = cur.b + 1 == cur.nv;
@@ -661,7 +682,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
         flush(bfirst, nst);
         nst = 0;
         bfirst = cur.b + 1;
-      } else if (nst == kPfStage) {
+      } else if ((cur.b & (kPfStage - 1)) == kPfStage - 1) {
         flush_due = true;
       }
       if (!last) {
@@ -673,7 +694,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
       }
     } else {
       ++tile_done;
-      if (nst == kPfStage || tile_end || last) {
+      if ((cur.b & (kPfStage - 1)) == kPfStage - 1 || tile_end || last) {
         flush(bfirst, nst);
         nst = 0;
         bfirst = cur.b + 1;
