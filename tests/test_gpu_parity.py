@@ -569,6 +569,24 @@ def test_graph_capture_replay_with_new_lengths():
         assert torch.equal(got, want), f"replay {it} differs from eager"
 
 
+@pytest.mark.parametrize("kfmt", [KFMT_BF16, KFMT_NVFP4], ids=["bf16", "nvfp4"])
+def test_prefill_unaligned_score_layout(kfmt):
+    """A score view whose base is 4 bytes past a 16-byte boundary and whose
+    row stride is odd cannot take the prefill write-out's 16-byte stores: the
+    entry-by-entry path gives the same scores and ids as an aligned tensor,
+    and touches nothing outside the visible entries."""
+    w = small(4, R=2, lens=(700, 1500), Q=333, max_seq_len=2048, kfmt=kfmt)
+    s_al, out_al = run_split(w)
+    big = torch.full((w.heads, w.rows, w.score_width + 3), float("nan"), device=DEV)
+    view = big[:, :, 1:1 + w.score_width]
+    assert view.data_ptr() % 16 == 4 and view.stride(1) % 4 == 3
+    _say(f"case unaligned score layout ({'nvfp4' if kfmt else 'bf16'})")
+    _, out_un = run_split(w, scores=view)
+    assert torch.equal(out_un, out_al)
+    assert torch.equal(view.contiguous().view(torch.int32), s_al.view(torch.int32))
+    assert bool(torch.isnan(big[:, :, 0]).all()) and bool(torch.isnan(big[:, :, 1 + w.score_width:]).all())
+
+
 def test_graph_capture_one_launch_small_batch():
     """The one-launch small-batch path captured once; replays after new
     device lengths and queries match eager calls and the two-launch
