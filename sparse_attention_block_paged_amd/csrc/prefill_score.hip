@@ -442,11 +442,14 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
       // NVFP4: lane (nl, kg) multiplies token 32tt + nl, dims 64kg + 8kk ..
       // +8 at k-step (tt, kk): nibble dword kk of the lane's half row
       // (chunks 2kg and 2kg + 1, words W0 for kk < 4 and W1 after), under
-      // scale byte kk / 2 of the token's scale word S (bytes 4kg .. 4kg + 3
-      // of its 8).  Each pair of k-steps takes one table entry L: the 8 E4M3
-      // codes of that scale, read two steps ahead.  W1 is read at kk = 0,
-      // the next tile's W0 at kk = 4, its S at kk = 0 and its first entry at
-      // kk = 6, so every read leads its use by two to six k-steps.
+      // scale byte kk / 2 of the token's scale word (bytes 4kg .. 4kg + 3 of
+      // its 8).  Each pair of k-steps takes one table entry: the 8 E4M3 codes
+      // of that scale.  The fragment of k-step st + 1 is decoded during k-step
+      // st, its vector instructions placed between st's four multiplies, so
+      // the matrix pipe is fed while the decode runs.  Reads lead their use:
+      // W1 is read at kk = 0 of its tile, the next tile's W0 at kk = 4 and its
+      // scale word at kk = 0, a pair's table entry three k-steps before the
+      // decode of its first k-step.
       const int sw = (nl >> 1) & 3;
       const uint32_t nb0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)(smem + kPfFp4Stage0 + slot * kFp4NibBytes);
       const uint32_t sb0 = (uint32_t)(uintptr_t)(const MM3_AS3 uint8_t*)(smem + kPfFp4Scale0 + slot * kFp4ScaleBytes);
@@ -462,30 +465,41 @@ __global__ __launch_bounds__(kPfThreads, kPfWgPerCu) void prefill_score_kernel(S
       auto ldl = [&](uint32_t sword, int p) {
         return *(const MM3_AS3 u32x2*)(uintptr_t)(lb0 + 8 * ((sword >> (8 * p)) & 0xFFu));
       };
-      u32x4 W0 = ldw(w0a, 0), W1{};
+      u32x4 W0 = ldw(w0a, 0), W1 = ldw(w1a, 0);
       uint32_t S = lds(0), Sn = 0;
+      // L[g & 1]: the entry of k-step pair g (k-steps 2g, 2g + 1 of the 32)
       u32x2 L[2];
       L[0] = ldl(S, 0);
-      L[1] = u32x2{0u, 0u};
+      L[1] = ldl(S, 1);
+      bf16x8 D = as_bf16x8(fp4x8_to_bf16(W0[0], L[0]));
 #pragma unroll
       for (int st = 0; st < 32; ++st) {
         const int tt = st >> 3, kk = st & 7;
-        if (kk == 0) {
-          W1 = ldw(w1a, tt);
-          if (tt + 1 < 4) Sn = lds(tt + 1);
-        }
+        if (kk == 0 && tt > 0) W1 = ldw(w1a, tt);
+        if (kk == 0 && tt + 1 < 4) Sn = lds(tt + 1);
         if (kk == 4 && tt + 1 < 4) W0 = ldw(w0a, tt + 1);
-        if ((kk & 1) == 0) {
-          if (kk < 6) {
-            L[((kk >> 1) + 1) & 1] = ldl(S, (kk >> 1) + 1);
-          } else if (tt + 1 < 4) {
-            S = Sn;
-            L[0] = ldl(S, 0);
-          }
+        // the entry of the pair that starts at k-step st + 3
+        if (((st + 3) & 1) == 0 && st + 3 < 32) {
+          const int t3 = st + 3;
+          L[(t3 >> 1) & 1] = ldl((t3 >> 3) == tt ? S : Sn, (t3 & 7) >> 1);
         }
-        const uint32_t x = kk < 4 ? W0[kk & 3] : W1[kk & 3];
-        multiply(as_bf16x8(fp4x8_to_bf16(x, L[(kk >> 1) & 1])), kk);
+        bf16x8 Dn = D;
+        if (st + 1 < 32) {
+          const int k1 = (st + 1) & 7;
+          const uint32_t x = k1 < 4 ? W0[k1 & 3] : W1[k1 & 3];
+          Dn = as_bf16x8(fp4x8_to_bf16(x, L[((st + 1) >> 1) & 1]));
+        }
+        multiply(D, kk);
+        // reads first, then each multiply followed by a share of the decode
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int q = 0; q < kPfQt; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
         if (kk == 7) tile_max(tt);
+        if (kk == 7) S = Sn;
+        D = Dn;
         __builtin_amdgcn_sched_barrier(0);
       }
     }
