@@ -220,12 +220,6 @@ ScoreArgs score_args(const mm3_problem* p, float* s, int64_t sh, int64_t sr) {
   return a;
 }
 
-// Launch policy.  A request with heads * n_r <= 16 rows goes to the decode
-// scorer (one MFMA tile of query rows, bandwidth-bound), a larger one to the
-// MFMA prefill scorer.  Uniform batches take one of them for every request.
-// Ragged batches may hold both kinds, so both launch, each taking only its
-// own requests (decided on the device from cu_seqlens_q); the decode one
-// sizes its query tile for the largest row count it can take.
 // Batches that mm3_index_decode scores and selects in one launch: every
 // request is a decode request (heads * query_len <= kDecodeRows) that sees at
 // most kSmallBlocks blocks, there are few enough of them for one workgroup
@@ -239,6 +233,12 @@ bool small_decode_ok(const mm3_problem* p, const float* scores_out, int64_t sh, 
   return !scores_out || score_args(p, const_cast<float*>(scores_out), sh, sr).s_bytes > 0;
 }
 
+// Launch policy.  A request with heads * n_r <= 16 rows goes to the decode
+// scorer (one MFMA tile of query rows, bandwidth-bound), a larger one to the
+// MFMA prefill scorer.  Uniform batches take one of them for every request.
+// Ragged batches may hold both kinds, so both launch, each taking only its
+// own requests (decided on the device from cu_seqlens_q); the decode one
+// sizes its query tile for the largest row count it can take.
 int launch_scores(const mm3_problem* p, float* s, int64_t sh, int64_t sr, hipStream_t st) {
   ScoreArgs a = score_args(p, s, sh, sr);
   const bool bf16 = p->kfmt == MM3_KFMT_BF16;
