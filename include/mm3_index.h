@@ -241,8 +241,8 @@ size_t mm3_index_decode_workspace_bytes(const mm3_problem* p, int32_t topk,
 
 /*
  * mm3_index_decode -- scores then top-k in one call (page "ops.index_topk",
- * minimax_m3_index_decode: "decode index block-score followed by fused
- * adaptive top-k selection", out written in place at a stable address).
+ * minimax_m3_index_decode: the decode block scores and the top-k selection
+ * of them in the same call, out written in place at a stable address).
  *   out / topk / init_blocks / local_blocks as in mm3_index_topk.
  *   scores_out  optional (NULL = keep scores in the workspace); when given it
  *               receives the scores exactly as mm3_index_score writes them.

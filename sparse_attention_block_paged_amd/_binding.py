@@ -193,7 +193,7 @@ def make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_sca
                  kscales=None, cu_seqlens_q=None, prefix_lens=None) -> Problem:
     """Marshal tensors into the C problem struct (no copies)."""
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != HEAD_DIM or q.stride(2) != 1:
-        raise ValueError("q must be bf16 [tokens, heads, 128] with contiguous D")
+        raise ValueError("q: expected bf16 of shape [tokens, heads, 128] with unit stride along the last dim")
     if kscales is None:
         if kdata.dtype != torch.bfloat16 or tuple(kdata.shape[1:]) != (BLOCK, HEAD_DIM) \
                 or not kdata.is_contiguous():
@@ -212,7 +212,7 @@ def make_problem(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm_sca
     rows = make_rows(seq_lens, query_len, max_seq_len, q.shape[0], cu_seqlens_q, prefix_lens)
     devs = {t.device for t in (q, kdata, block_table, seq_lens) + ((kscales,) if kscales is not None else ())}
     if len(devs) != 1:
-        raise ValueError("all score inputs must be on the same device")
+        raise ValueError("q, the index cache, the block table and the lengths have to share one device")
     p = Problem()
     p.q = q.data_ptr()
     p.q_tok_stride = q.stride(0)
@@ -334,7 +334,7 @@ def mm3_index_decode(q, kdata, block_table, seq_lens, query_len, max_seq_len, sm
     sp_args = (attention_block_table, sparse_block_table_out, sparse_context_lens_out,
                pages_per_block, block_page_stride)
     if any(x is not None for x in sp_args) and any(x is None for x in sp_args):
-        raise ValueError("sparse-table arguments must be provided together")
+        raise ValueError("the sparse-table arguments go together: pass all of them or none")
     sparse = None
     if attention_block_table is not None:
         sparse = make_sparse_out(attention_block_table, pages_per_block, block_page_stride,
@@ -415,7 +415,7 @@ def mm3_index_decode_static(q, kdata, block_table, seq_lens, query_len, max_seq_
     sp_args = (attention_block_table, sparse_block_table_out, sparse_context_lens_out,
                pages_per_block, block_page_stride)
     if any(x is not None for x in sp_args) and any(x is None for x in sp_args):
-        raise ValueError("sparse-table arguments must be provided together")
+        raise ValueError("the sparse-table arguments go together: pass all of them or none")
     sparse = None
     if attention_block_table is not None:
         sparse = make_sparse_out(attention_block_table, pages_per_block, block_page_stride,

@@ -146,7 +146,7 @@ int check_out(int32_t* out, int64_t oh, int64_t orow, int32_t heads, int64_t T, 
 // the attention table wide enough for every block).
 int check_sparse(const mm3_sparse_out* s, const mm3_rows* rows, int32_t topk, int32_t heads) {
   if (!s->attention_block_table || !s->sparse_table || !s->sparse_ctx_lens)
-    return fail(MM3_EINVAL, "sparse-table arguments must be provided together (non-NULL)");
+    return fail(MM3_EINVAL, "the sparse-table arguments go together: all of them non-NULL");
   if (heads != 1)
     return fail(MM3_EINVAL, "the sparse block table is built for one index head, got %d", heads);
   const int32_t P = s->pages_per_block;
@@ -613,7 +613,7 @@ int mm3_index_decode_static(const mm3_problem* p, int32_t topk, int32_t init_blo
 int mm3_build_sparse_block_table(const int32_t* topk_idx, int64_t o_row_stride, int32_t topk,
                                  const mm3_rows* rows, const mm3_sparse_out* sparse, void* stream) {
   if (!topk_idx || !sparse)
-    return fail(MM3_EINVAL, "sparse-table arguments must be provided together (non-NULL)");
+    return fail(MM3_EINVAL, "the sparse-table arguments go together: all of them non-NULL");
   if (topk < 1 || topk > MM3_MAX_TOPK) return fail(MM3_EINVAL, "topk must be in [1, 1024]");
   int rc = check_rows(rows, 0);
   if (rc) return rc;
