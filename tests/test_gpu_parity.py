@@ -775,8 +775,9 @@ def test_full_size_mixed_serving(oracle_pool):
 
 # ------------------------------------------------- fused sparse block table
 #
-# page "ops.index_topk", minimax_m3_index_decode: the optional sparse-table
-# arguments fuse table construction into the selector (one index head).
+# page "ops.index_topk", minimax_m3_index_decode: given the table arguments,
+# the selector builds the sparse block table as it writes the ids (one index
+# head).
 
 FUSED_SPARSE = [
     # (label, make kwargs, pages per block, page stride)
